@@ -1,0 +1,159 @@
+"""Python binding of the gfx950 dense GEMM library (libdg.so, C ABI in include/dg.h).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch provides the device memory and the current stream.
+
+    import dense_gemm_19_amd as dg
+    dg.gemm(A, B, C, alpha=1.0, beta=0.0)                     # C <- alpha*A@B + beta*C
+    dg.gemm_fp8(qA, sA, qB, sB, C, alpha=1.0, beta=0.0)       # block-scaled E4M3
+    print(dg.plan(A, B, C))                                    # the chosen plan, no launch
+
+Tensors may have any strides (transposes, padded rows, up to 4-D views whose
+leading dims merge into one row stride); views are passed as pointer + shape +
+byte strides, nothing is copied or made contiguous.  The library is loaded from
+this directory; if it is missing, every call raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+# dg_dtype codes
+DG_F32, DG_F16, DG_BF16, DG_F8E4M3 = 0, 1, 2, 3
+_DTYPE = {torch.float32: DG_F32, torch.float16: DG_F16, torch.bfloat16: DG_BF16,
+          torch.float8_e4m3fn: DG_F8E4M3}
+
+STATUS = ["DG_SUCCESS", "DG_ERR_NULL", "DG_ERR_NDIM", "DG_ERR_STRIDE", "DG_ERR_SHAPE_MISMATCH",
+          "DG_ERR_DTYPE", "DG_ERR_MISALIGNED", "DG_ERR_ALIAS", "DG_ERR_NONFINITE_SCALAR",
+          "DG_ERR_OVERFLOW", "DG_ERR_UNSUPPORTED_VIEW", "DG_ERR_POINTER", "DG_ERR_ARCH",
+          "DG_ERR_HIP", "DG_ERR_INVALID_ARG"]
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else f"status {status}"
+        super().__init__(f"{where}: {name}" if where else name)
+
+
+class View(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m dense_gemm_19_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(View)
+        L.dg_gemm.argtypes = [P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_fp8.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_plan.argtypes = [P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_char_p,
+                                   ctypes.c_size_t]
+        L.dg_gemm_fp8_plan.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_char_p, ctypes.c_size_t]
+        for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dg_status_str.argtypes = [ctypes.c_int]
+        L.dg_status_str.restype = ctypes.c_char_p
+        L.dg_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def make_view(ptr: int, shape, byte_strides, dtype_code: int) -> View:
+    """A dg_view from raw geometry (pointer value, extents, byte strides)."""
+    if len(shape) != len(byte_strides):
+        raise ValueError("shape and strides differ in length")
+    v = View()
+    v.ptr = ptr
+    v.ndim = len(shape)
+    for d in range(min(len(shape), 4)):
+        v.shape[d] = int(shape[d])
+        v.stride[d] = int(byte_strides[d])
+    v.dtype = dtype_code
+    return v
+
+
+def view_of(t: torch.Tensor) -> View:
+    """A dg_view of a tensor: data_ptr, shape, strides * element size, dtype."""
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() == 0:
+        t = t.reshape(1)
+    es = t.element_size()
+    return make_view(t.data_ptr(), tuple(t.shape), tuple(s * es for s in t.stride()), _DTYPE[t.dtype])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise DGError(st, where)
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, alpha: float = 1.0, beta: float = 0.0,
+         stream=None) -> torch.Tensor:
+    """C <- alpha * A @ B + beta * C on the current (or given) stream; returns C."""
+    va, vb, vc = view_of(A), view_of(B), view_of(C)
+    _check(lib().dg_gemm(ctypes.byref(va), ctypes.byref(vb), ctypes.byref(vc), alpha, beta,
+                         _stream(stream)), "dg_gemm")
+    return C
+
+
+def gemm_fp8(A: torch.Tensor, A_scale: torch.Tensor, B: torch.Tensor, B_scale: torch.Tensor,
+             C: torch.Tensor, alpha: float = 1.0, beta: float = 0.0, stream=None) -> torch.Tensor:
+    """C <- alpha * (qA*sA) @ (qB*sB) + beta * C with 1x128 / 128x128 block scales; returns C."""
+    vs = [view_of(t) for t in (A, A_scale, B, B_scale, C)]
+    _check(lib().dg_gemm_fp8(*[ctypes.byref(v) for v in vs], alpha, beta, _stream(stream)),
+           "dg_gemm_fp8")
+    return C
+
+
+def plan_views(A: View, B: View, C: View, alpha: float = 1.0, beta: float = 0.0,
+               A_scale: View | None = None, B_scale: View | None = None) -> tuple[int, str]:
+    """(status, plan text) for raw views, without launching anything."""
+    buf = ctypes.create_string_buffer(1024)
+    if A_scale is None and B_scale is None:
+        st = lib().dg_gemm_plan(ctypes.byref(A), ctypes.byref(B), ctypes.byref(C), alpha, beta,
+                                buf, len(buf))
+    else:
+        st = lib().dg_gemm_fp8_plan(ctypes.byref(A), ctypes.byref(A_scale), ctypes.byref(B),
+                                    ctypes.byref(B_scale), ctypes.byref(C), alpha, beta, buf, len(buf))
+    return st, buf.value.decode()
+
+
+def plan(A, B, C, alpha: float = 1.0, beta: float = 0.0, A_scale=None, B_scale=None) -> str:
+    """Describe the plan dg_gemm / dg_gemm_fp8 would run for these tensors."""
+    st, text = plan_views(view_of(A), view_of(B), view_of(C), alpha, beta,
+                          None if A_scale is None else view_of(A_scale),
+                          None if B_scale is None else view_of(B_scale))
+    _check(st, "dg_gemm_plan")
+    return text
+
+
+def status_str(st: int) -> str:
+    return lib().dg_status_str(st).decode()
+
+
+def version() -> int:
+    return lib().dg_version()

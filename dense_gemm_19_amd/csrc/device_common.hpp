@@ -1,0 +1,64 @@
+// device_common.hpp -- gfx950 device helpers: vector types, output conversion,
+// the alpha/beta epilogue store.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace dg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Generic pointer into LDS -> LDS address-space pointer (an addrspacecast).
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(3))) T *as_lds(const char *p) {
+    return (__attribute__((address_space(3))) T *)(const_cast<char *>(p));
+}
+
+// FP32 -> output element, round to nearest even (the hardware conversions on
+// gfx950 round to nearest even and keep NaN a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = static_cast<_Float16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+__device__ __forceinline__ float load_out(const char *p, int kind) {
+    if (kind == OUT_F32) return *reinterpret_cast<const float *>(p);
+    uint16_t b = *reinterpret_cast<const uint16_t *>(p);
+    return kind == OUT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+__device__ __forceinline__ void store_out(char *p, int kind, float v) {
+    if (kind == OUT_F32) *reinterpret_cast<float *>(p) = v;
+    else if (kind == OUT_BF16) *reinterpret_cast<uint16_t *>(p) = f32_to_bf16_bits(v);
+    else *reinterpret_cast<uint16_t *>(p) = f32_to_f16_bits(v);
+}
+
+// out = alpha * acc + beta * C_in (C_in read only when beta != 0), rounded to the
+// C dtype and stored at (m, n).  The caller has checked m < M and n < N.
+__device__ __forceinline__ void epilogue_store(const Epilogue &e, int64_t m, int64_t n, float acc) {
+    char *p = e.C + m * e.c_rs + n * e.c_cs;
+    float v = e.alpha * acc;
+    if (e.beta != 0.0f) v = fmaf(e.beta, load_out(p, e.out_kind), v);
+    store_out(p, e.out_kind, v);
+}
+
+}  // namespace dg

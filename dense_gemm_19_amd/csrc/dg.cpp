@@ -1,0 +1,300 @@
+// dg.cpp -- the C ABI: validation, device checks, plan lookup and launch.
+//
+// Every argument is validated before anything is enqueued, so an error return
+// leaves C untouched (kwkr.cn view-native GEMM article, sections 4.1-4.3 and
+// its troubleshooting table in 5.1: shape agreement, byte strides, 64-bit
+// offsets, NaN/Inf alpha/beta, device pointers, thread-safe kernel caching).
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "dg.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "view.hpp"
+
+namespace dg {
+namespace {
+
+bool env_on(const char *name) {
+    const char *s = std::getenv(name);
+    return s && s[0] == '1';
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+dg_status validate(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
+                   const dg_view *C, float alpha, float beta, bool fp8, Problem *out) {
+    Problem p;
+    p.fp8 = fp8;
+    dg_status st;
+    if ((st = canonicalize(A, &p.A)) != DG_SUCCESS) return st;
+    if (fp8 && (st = canonicalize(SA, &p.SA)) != DG_SUCCESS) return st;
+    if ((st = canonicalize(B, &p.B)) != DG_SUCCESS) return st;
+    if (fp8 && (st = canonicalize(SB, &p.SB)) != DG_SUCCESS) return st;
+    if ((st = canonicalize(C, &p.C)) != DG_SUCCESS) return st;
+
+    // dtypes
+    if (fp8) {
+        if (p.A.dtype != DG_F8E4M3 || p.B.dtype != DG_F8E4M3) return DG_ERR_DTYPE;
+        if (p.SA.dtype != DG_F32 || p.SB.dtype != DG_F32) return DG_ERR_DTYPE;
+        p.in_kind = IN_F8;
+    } else {
+        if (p.A.dtype != DG_F16 && p.A.dtype != DG_BF16) return DG_ERR_DTYPE;
+        if (p.B.dtype != p.A.dtype) return DG_ERR_DTYPE;
+        p.in_kind = p.A.dtype == DG_F16 ? IN_F16 : IN_BF16;
+    }
+    switch (p.C.dtype) {
+    case DG_F32: p.out_kind = OUT_F32; break;
+    case DG_F16: p.out_kind = OUT_F16; break;
+    case DG_BF16: p.out_kind = OUT_BF16; break;
+    default: return DG_ERR_DTYPE;
+    }
+
+    // shapes: A M x K, B K x N, C M x N
+    p.M = p.A.rows;
+    p.K = p.A.cols;
+    p.N = p.B.cols;
+    if (p.B.rows != p.K || p.C.rows != p.M || p.C.cols != p.N) return DG_ERR_SHAPE_MISMATCH;
+    if (fp8) {
+        const int64_t KB = cdiv(p.K, 128), NB = cdiv(p.N, 128);
+        if (p.SA.rows != p.M || p.SA.cols != KB) return DG_ERR_SHAPE_MISMATCH;
+        if (p.SB.rows != KB || p.SB.cols != NB) return DG_ERR_SHAPE_MISMATCH;
+    }
+    // kernels index M, N and K with 32-bit integers
+    if (p.M > INT32_MAX || p.N > INT32_MAX || p.K > INT32_MAX) return DG_ERR_OVERFLOW;
+
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return DG_ERR_NONFINITE_SCALAR;
+    p.alpha = alpha;
+    p.beta = beta;
+
+    // C is written: it must not overlap itself or any input.
+    if (self_overlaps(p.C)) return DG_ERR_STRIDE;
+    if (spans_overlap(p.C, p.A) || spans_overlap(p.C, p.B)) return DG_ERR_ALIAS;
+    if (fp8 && (spans_overlap(p.C, p.SA) || spans_overlap(p.C, p.SB))) return DG_ERR_ALIAS;
+    *out = p;
+    return DG_SUCCESS;
+}
+
+// Current device description, cached per device id.
+struct DevCache {
+    std::mutex mu;
+    bool known[64] = {};
+    Device dev[64];
+};
+
+DevCache &devcache() {
+    static DevCache c;
+    return c;
+}
+
+dg_status current_device(Device *d, bool require) {
+    int id = 0;
+    if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= 64) {
+        (void)hipGetLastError();
+        if (require) return DG_ERR_HIP;
+        *d = Device();
+        return DG_SUCCESS;
+    }
+    DevCache &c = devcache();
+    std::lock_guard<std::mutex> g(c.mu);
+    if (!c.known[id]) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, id) != hipSuccess) {
+            (void)hipGetLastError();
+            if (require) return DG_ERR_HIP;
+            *d = Device();
+            return DG_SUCCESS;
+        }
+        Device x;
+        x.present = true;
+        std::snprintf(x.arch, sizeof x.arch, "%s", prop.gcnArchName);
+        x.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        x.cus = prop.multiProcessorCount;
+        x.lds_bytes = (int)prop.sharedMemPerBlock;
+        c.dev[id] = x;
+        c.known[id] = true;
+    }
+    *d = c.dev[id];
+    return DG_SUCCESS;
+}
+
+dg_status check_pointer(const void *p) {
+    if (!p) return DG_SUCCESS;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_POINTER;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return DG_ERR_POINTER;
+    return DG_SUCCESS;
+}
+
+Epilogue make_epi(const Problem &p) {
+    Epilogue e;
+    e.C = const_cast<char *>(p.C.ptr);
+    e.c_rs = p.C.rs;
+    e.c_cs = p.C.cs;
+    e.out_kind = p.out_kind;
+    e.alpha = p.alpha;
+    e.beta = p.beta;
+    return e;
+}
+
+dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
+    const Plan pl = cached_plan(p, d);
+    const Epilogue epi = make_epi(p);
+    if (pl.path == Path::Noop) return DG_SUCCESS;
+    if (pl.path == Path::Scale) {
+        ScaleArgs s{epi, (int)p.M, (int)p.N};
+        return launch_scale(s, stream) == hipSuccess ? DG_SUCCESS : DG_ERR_HIP;
+    }
+    float *ws = nullptr;
+    if (pl.splits > 1) {
+        if (hipMallocAsync(reinterpret_cast<void **>(&ws), pl.ws_bytes, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return DG_ERR_HIP;
+        }
+    }
+    hipError_t e;
+    if (pl.path == Path::Skinny) {
+        SkinnyArgs a;
+        a.A = p.A.ptr; a.a_rs = p.A.rs; a.a_cs = p.A.cs;
+        a.B = p.B.ptr; a.b_rs = p.B.rs; a.b_cs = p.B.cs;
+        a.epi = epi;
+        a.ws = ws;
+        a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+        a.in_kind = p.in_kind;
+        a.a_vec = pl.sk_a_vec;
+        a.splits = pl.splits;
+        a.k_per_split = pl.sk_k_per_split;
+        e = launch_skinny(pl.sk_kind, pl.sk_mmax, a, pl.sk_grid_x, stream);
+    } else {
+        MfmaArgs a;
+        a.a = Operand{p.A.ptr, pl.a.r_stride, pl.a.k_stride, pl.a.vec ? 1 : 0};
+        a.b = Operand{p.B.ptr, pl.b.r_stride, pl.b.k_stride, pl.b.vec ? 1 : 0};
+        a.sa = p.fp8 ? reinterpret_cast<const float *>(p.SA.ptr) : nullptr;
+        a.sa_rs = p.SA.rs; a.sa_cs = p.SA.cs;
+        a.sb = p.fp8 ? reinterpret_cast<const float *>(p.SB.ptr) : nullptr;
+        a.sb_rs = p.SB.rs; a.sb_cs = p.SB.cs;
+        a.epi = epi;
+        a.ws = ws;
+        a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+        a.tiles_m = pl.tiles_m; a.tiles_n = pl.tiles_n;
+        a.ktiles = pl.ktiles;
+        a.kt_per_split = pl.kt_per_split;
+        a.splits = pl.splits;
+        a.group_m = pl.group_m;
+        e = launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
+    }
+    if (e == hipSuccess && pl.splits > 1) {
+        ReduceArgs r{ws, epi, (int)p.M, (int)p.N, pl.splits};
+        e = launch_reduce(r, stream);
+    }
+    if (ws) {
+        if (hipFreeAsync(ws, stream) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    if (env_on("DG_SYNC_DEBUG")) {
+        if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return DG_ERR_HIP;
+    }
+    return DG_SUCCESS;
+}
+
+dg_status entry(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
+                const dg_view *C, float alpha, float beta, bool fp8, hipStream_t stream) {
+    Problem p;
+    dg_status st = validate(A, SA, B, SB, C, alpha, beta, fp8, &p);
+    if (st != DG_SUCCESS) return st;
+    Device d;
+    if ((st = current_device(&d, true)) != DG_SUCCESS) return st;
+    if (!d.gfx950) return DG_ERR_ARCH;
+    if (env_on("DG_CHECK_POINTERS")) {
+        const Mat *ms[] = {&p.A, &p.B, &p.C, fp8 ? &p.SA : nullptr, fp8 ? &p.SB : nullptr};
+        for (const Mat *m : ms)
+            if (m && !m->empty() && (st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
+    }
+    return run(p, d, stream);
+}
+
+dg_status plan_entry(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
+                     const dg_view *C, float alpha, float beta, bool fp8, char *buf, size_t len) {
+    if (!buf && len) return DG_ERR_INVALID_ARG;
+    Problem p;
+    dg_status st = validate(A, SA, B, SB, C, alpha, beta, fp8, &p);
+    if (st != DG_SUCCESS) return st;
+    Device d;
+    int count = 0;
+    if (hipGetDeviceCount(&count) == hipSuccess && count > 0) {
+        if ((st = current_device(&d, false)) != DG_SUCCESS) return st;
+    } else {
+        (void)hipGetLastError();
+        d = Device();
+    }
+    const Plan pl = select_plan(p, d);
+    if (len) {
+        const std::string s = describe(p, pl, d);
+        std::snprintf(buf, len, "%s", s.c_str());
+    }
+    if (d.present && !d.gfx950) return DG_ERR_ARCH;
+    return DG_SUCCESS;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,
+                  hipStream_t stream) {
+    return dg::entry(A, nullptr, B, nullptr, C, alpha, beta, false, stream);
+}
+
+dg_status dg_gemm_fp8(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                      const dg_view *B_scale, const dg_view *C, float alpha, float beta,
+                      hipStream_t stream) {
+    return dg::entry(A, A_scale, B, B_scale, C, alpha, beta, true, stream);
+}
+
+dg_status dg_gemm_plan(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,
+                       char *buf, size_t len) {
+    return dg::plan_entry(A, nullptr, B, nullptr, C, alpha, beta, false, buf, len);
+}
+
+dg_status dg_gemm_fp8_plan(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                           const dg_view *B_scale, const dg_view *C, float alpha, float beta, char *buf,
+                           size_t len) {
+    return dg::plan_entry(A, A_scale, B, B_scale, C, alpha, beta, true, buf, len);
+}
+
+const char *dg_status_str(dg_status s) {
+    switch (s) {
+    case DG_SUCCESS: return "DG_SUCCESS";
+    case DG_ERR_NULL: return "DG_ERR_NULL";
+    case DG_ERR_NDIM: return "DG_ERR_NDIM";
+    case DG_ERR_STRIDE: return "DG_ERR_STRIDE";
+    case DG_ERR_SHAPE_MISMATCH: return "DG_ERR_SHAPE_MISMATCH";
+    case DG_ERR_DTYPE: return "DG_ERR_DTYPE";
+    case DG_ERR_MISALIGNED: return "DG_ERR_MISALIGNED";
+    case DG_ERR_ALIAS: return "DG_ERR_ALIAS";
+    case DG_ERR_NONFINITE_SCALAR: return "DG_ERR_NONFINITE_SCALAR";
+    case DG_ERR_OVERFLOW: return "DG_ERR_OVERFLOW";
+    case DG_ERR_UNSUPPORTED_VIEW: return "DG_ERR_UNSUPPORTED_VIEW";
+    case DG_ERR_POINTER: return "DG_ERR_POINTER";
+    case DG_ERR_ARCH: return "DG_ERR_ARCH";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+    case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
+    }
+    return "DG_ERR_UNKNOWN";
+}
+
+int dg_version(void) { return DG_VERSION; }
+
+}  // extern "C"

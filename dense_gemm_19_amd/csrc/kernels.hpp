@@ -1,0 +1,95 @@
+// kernels.hpp -- argument blocks and launchers shared by the host code and the
+// gfx950 kernels.  All strides are in bytes.
+#pragma once
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace dg {
+
+// Operand storage modes inside a K tile.
+//  KMAJ : the operand is stored K-contiguous (A row-major, or B given as B^T
+//         row-major).  LDS holds [rows][128 bytes of K]; fragments are plain
+//         16-byte LDS reads.
+//  MNMAJ: the operand is stored M- or N-contiguous (B row-major [K][N], or A
+//         column-major).  LDS holds [K][rows]; fragments come from the gfx950
+//         LDS transpose reads (ds_read_b64_tr_b16 / ds_read_b64_tr_b8).
+enum OpMode : int { KMAJ = 0, MNMAJ = 1 };
+
+// Input element kinds of the matrix-core path.
+enum InKind : int { IN_F16 = 0, IN_BF16 = 1, IN_F8 = 2 };
+
+// Output element kinds (match dg_dtype numbering for F32/F16/BF16).
+enum OutKind : int { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
+
+struct Operand {
+    const char *ptr;
+    int64_t r_stride;   // bytes per step of the operand's M (A) or N (B) index
+    int64_t k_stride;   // bytes per step of K
+    int vec;            // 1: 16-byte vector loads are legal for full chunks
+};
+
+struct Epilogue {
+    char *C;
+    int64_t c_rs, c_cs; // bytes
+    int out_kind;       // OutKind
+    float alpha, beta;  // beta == 0: C is not read
+};
+
+struct MfmaArgs {
+    Operand a, b;               // a: M x K, b: N x K (as "rows x K")
+    const float *sa; int64_t sa_rs, sa_cs;   // FP8 only: [M][KB] scales (bytes)
+    const float *sb; int64_t sb_rs, sb_cs;   // FP8 only: [KB][NB] scales (bytes)
+    Epilogue epi;
+    float *ws;                  // split-K partials [S][M][N] FP32, or null when S == 1
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int ktiles;                 // ceil(K / BK)
+    int kt_per_split;           // K tiles handled by one grid.z slice
+    int splits;                 // S
+    int group_m;                // tile raster: group of tile rows walked together
+};
+
+struct SkinnyArgs {
+    const char *A; int64_t a_rs, a_cs;   // M x K
+    const char *B; int64_t b_rs, b_cs;   // K x N
+    Epilogue epi;
+    float *ws;                            // [S][M][N] partials when S > 1
+    int M, N, K;
+    int in_kind;                          // IN_F16 / IN_BF16
+    int a_vec;                            // SK_BK: A rows K-contiguous and 16-byte aligned
+    int splits;                           // S
+    int k_per_split;                      // rows of K per split (multiple of 8)
+};
+
+struct ReduceArgs {
+    const float *ws;    // [S][M][N]
+    Epilogue epi;
+    int M, N, S;
+};
+
+struct ScaleArgs {      // C <- beta * C (beta == 0: C <- 0), for alpha == 0 or K == 0
+    Epilogue epi;
+    int M, N;
+};
+
+// Tile configurations of the matrix-core kernel (index = MfmaTile).
+enum MfmaTile : int { T256x256 = 0, T128x128 = 1, T64x64 = 2, T128x64 = 3, NUM_MFMA_TILES = 4 };
+inline int mfma_tile_bm(int t) { const int v[] = {256, 128, 64, 128}; return v[t]; }
+inline int mfma_tile_bn(int t) { const int v[] = {256, 128, 64, 64}; return v[t]; }
+// LDS bytes: two stages of (BM + BN) rows x 128 bytes of K (+ BM FP32 row scales for FP8).
+inline int mfma_tile_lds(int t, bool fp8) {
+    return 2 * ((mfma_tile_bm(t) + mfma_tile_bn(t)) * 128 + (fp8 ? mfma_tile_bm(t) * 4 : 0));
+}
+
+// Skinny (M <= 8) variants.
+enum SkinnyKind : int { SK_BN = 0 /* B N-contiguous */, SK_BK = 1 /* B K-contiguous */ };
+
+// slow != 0 selects the element-wise loader (any strides, any K) on a 64x64 tile.
+hipError_t launch_mfma(int in_kind, int tile, int a_mode, int b_mode, int slow,
+                       const MfmaArgs &args, hipStream_t stream);
+hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
+hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,259 @@
+// plan.cpp -- see plan.hpp.
+#include "plan.hpp"
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+namespace dg {
+namespace {
+
+struct Overrides {
+    int force_path = 0;    // 0 none, 1 skinny, 2 mfma
+    int force_splitk = 0;
+    int force_tile = -1;
+    bool no_vec = false;
+    bool log = false;
+};
+
+const Overrides &overrides() {
+    static const Overrides o = [] {
+        Overrides r;
+        if (const char *s = std::getenv("DG_FORCE_PATH")) {
+            if (!std::strcmp(s, "skinny")) r.force_path = 1;
+            else if (!std::strcmp(s, "mfma")) r.force_path = 2;
+        }
+        if (const char *s = std::getenv("DG_FORCE_SPLITK")) r.force_splitk = std::atoi(s);
+        if (const char *s = std::getenv("DG_FORCE_TILE")) {
+            for (int t = 0; t < NUM_MFMA_TILES; ++t) {
+                char name[32];
+                std::snprintf(name, sizeof name, "%dx%d", mfma_tile_bm(t), mfma_tile_bn(t));
+                if (!std::strcmp(s, name)) r.force_tile = t;
+            }
+        }
+        if (const char *s = std::getenv("DG_NO_VEC")) r.no_vec = s[0] == '1';
+        if (const char *s = std::getenv("DG_LOG")) r.log = s[0] == '1';
+        return r;
+    }();
+    return o;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A as an M x K operand ("rows" = M).
+OperandPlan plan_a(const Mat &A, int64_t M, int64_t K, int epc) {
+    OperandPlan o;
+    if (A.cols_contig()) {
+        o.mode = KMAJ; o.r_stride = A.rs; o.k_stride = A.cs;
+        o.vec = A.align_ptr >= 16 && (M <= 1 || A.align_rs >= 16) && K % epc == 0 && A.cs == A.esize;
+    } else if (A.rows_contig()) {
+        o.mode = MNMAJ; o.r_stride = A.rs; o.k_stride = A.cs;
+        o.vec = A.align_ptr >= 16 && (K <= 1 || A.align_cs >= 16) && M % epc == 0 && A.rs == A.esize;
+    } else {
+        o.mode = KMAJ; o.r_stride = A.rs; o.k_stride = A.cs; o.vec = false;
+    }
+    return o;
+}
+
+// B (K x N) as an N x K operand ("rows" = N).
+OperandPlan plan_b(const Mat &B, int64_t N, int64_t K, int epc) {
+    OperandPlan o;
+    if (B.rows_contig() && !(B.cols_contig() && K <= 1)) {
+        o.mode = KMAJ; o.r_stride = B.cs; o.k_stride = B.rs;
+        o.vec = B.align_ptr >= 16 && (N <= 1 || B.align_cs >= 16) && K % epc == 0 && B.rs == B.esize;
+    } else if (B.cols_contig()) {
+        o.mode = MNMAJ; o.r_stride = B.cs; o.k_stride = B.rs;
+        o.vec = B.align_ptr >= 16 && (K <= 1 || B.align_rs >= 16) && N % epc == 0 && B.cs == B.esize;
+    } else {
+        o.mode = KMAJ; o.r_stride = B.cs; o.k_stride = B.rs; o.vec = false;
+    }
+    return o;
+}
+
+bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
+    if (p.fp8 || p.M > 8) return false;
+    const Mat &A = p.A, &B = p.B;
+    const int mmax = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
+    const bool no_vec = overrides().no_vec;
+    // B N-contiguous: stream rows of B with 16-byte loads.
+    if (!no_vec && B.cols_contig() && B.cs == B.esize && B.align_ptr >= 16 && (p.K <= 1 || B.align_rs >= 16)) {
+        pl.sk_kind = SK_BN;
+        pl.sk_grid_x = (int)cdiv(p.N, 64);
+        const int64_t kmax_lds = 8192 / mmax;            // A slice <= 32 KB of LDS
+        int64_t S = cdiv(4LL * d.cus, pl.sk_grid_x);
+        S = std::min<int64_t>(S, std::max<int64_t>(1, p.K / 256));
+        S = std::max<int64_t>(S, cdiv(p.K, kmax_lds));
+        if (overrides().force_splitk > 0) S = overrides().force_splitk;
+        S = std::max<int64_t>(1, std::min<int64_t>(S, std::max<int64_t>(1, p.K)));
+        int64_t kps = cdiv(std::max<int64_t>(p.K, 1), S);
+        kps = cdiv(kps, 8) * 8;
+        if (kps > kmax_lds) return false;
+        pl.sk_k_per_split = (int)kps;
+        pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
+        pl.sk_mmax = mmax;
+        pl.lds_bytes = (int)std::max<int64_t>(kps * mmax * 4, 4LL * mmax * 64 * 4);
+        return true;
+    }
+    // B K-contiguous (e.g. a transposed cache): one wave per column.
+    if (!no_vec && B.rows_contig() && B.rs == B.esize && B.align_ptr >= 16 && (p.N <= 1 || B.align_cs >= 16)) {
+        pl.sk_kind = SK_BK;
+        pl.sk_grid_x = (int)cdiv(p.N, 4);
+        int64_t S = 1;
+        if (overrides().force_splitk > 0) S = overrides().force_splitk;
+        int64_t kps = cdiv(cdiv(std::max<int64_t>(p.K, 1), S), 8) * 8;
+        pl.sk_k_per_split = (int)kps;
+        pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
+        pl.sk_mmax = mmax;
+        pl.sk_a_vec = A.cols_contig() && A.cs == A.esize && A.align_ptr >= 16 && (p.M <= 1 || A.align_rs >= 16);
+        pl.lds_bytes = 0;
+        return true;
+    }
+    return false;
+}
+
+void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
+    const int epc = p.fp8 ? 16 : 8;              // elements per 16-byte chunk
+    const int kel = p.fp8 ? 128 : 64;            // K elements per tile
+    pl.path = Path::Mfma;
+    pl.a = plan_a(p.A, p.M, p.K, epc);
+    pl.b = plan_b(p.B, p.N, p.K, epc);
+    if (overrides().no_vec) pl.a.vec = pl.b.vec = false;
+    pl.slow = !(pl.a.vec && pl.b.vec);
+    pl.ktiles = (int)cdiv(p.K, kel);
+    int tile = T64x64;
+    if (!pl.slow) {
+        const int order[] = {T256x256, T128x128, T128x64, T64x64};
+        int best = T64x64;
+        int64_t best_tiles = -1;
+        bool found = false;
+        for (int t : order) {
+            const int64_t tm = cdiv(p.M, mfma_tile_bm(t)), tn = cdiv(p.N, mfma_tile_bn(t));
+            const int64_t nt = tm * tn;
+            // skip macro tiles that would be more than a quarter padding
+            const double eff = (double)p.M * (double)p.N /
+                               ((double)tm * mfma_tile_bm(t) * (double)tn * mfma_tile_bn(t));
+            if (eff < 0.75 && t != T64x64) continue;
+            if (nt >= d.cus) { tile = t; found = true; break; }
+            if (nt > best_tiles) { best_tiles = nt; best = t; }
+        }
+        if (!found) tile = best;
+        if (overrides().force_tile >= 0) tile = overrides().force_tile;
+    }
+    pl.tile = tile;
+    pl.tiles_m = (int)cdiv(p.M, mfma_tile_bm(tile));
+    pl.tiles_n = (int)cdiv(p.N, mfma_tile_bn(tile));
+    const int64_t nt = (int64_t)pl.tiles_m * pl.tiles_n;
+    int64_t S = 1;
+    if (nt < d.cus) S = std::min<int64_t>(cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2));
+    S = std::min<int64_t>(S, 16);
+    if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, std::max(pl.ktiles, 1));
+    S = std::max<int64_t>(S, 1);
+    pl.kt_per_split = (int)cdiv(std::max(pl.ktiles, 1), S);
+    pl.splits = (int)cdiv(std::max(pl.ktiles, 1), pl.kt_per_split);
+    pl.group_m = std::min(pl.tiles_m, 4);
+    pl.lds_bytes = mfma_tile_lds(pl.slow ? T64x64 : tile, p.fp8);
+}
+
+}  // namespace
+
+Plan select_plan(const Problem &p, const Device &d) {
+    Plan pl;
+    if (p.M == 0 || p.N == 0) { pl.path = Path::Noop; return pl; }
+    if (p.alpha == 0.0f || p.K == 0) { pl.path = Path::Scale; return pl; }
+    const int fp = overrides().force_path;
+    if (fp != 2 && skinny_ok(p, pl, d)) {
+        pl.path = Path::Skinny;
+    } else {
+        pl = Plan();
+        plan_mfma(p, pl, d);
+    }
+    pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
+    return pl;
+}
+
+namespace {
+
+struct Key {
+    int64_t M, N, K;
+    int64_t ars, acs, brs, bcs;
+    int fp8, in_kind, out_kind, scale_only;
+    int aal, bal, aalr, aalc, balr, balc;
+    int cus;
+    bool operator==(const Key &o) const { return std::memcmp(this, &o, sizeof(Key)) == 0; }
+};
+
+struct KeyHash {
+    size_t operator()(const Key &k) const {
+        const unsigned char *b = reinterpret_cast<const unsigned char *>(&k);
+        size_t h = 1469598103934665603ull;
+        for (size_t i = 0; i < sizeof(Key); ++i) h = (h ^ b[i]) * 1099511628211ull;
+        return h;
+    }
+};
+
+}  // namespace
+
+Plan cached_plan(const Problem &p, const Device &d) {
+    Key k;
+    std::memset(&k, 0, sizeof k);
+    k.M = p.M; k.N = p.N; k.K = p.K;
+    k.ars = p.A.rs; k.acs = p.A.cs; k.brs = p.B.rs; k.bcs = p.B.cs;
+    k.fp8 = p.fp8; k.in_kind = p.in_kind; k.out_kind = p.out_kind;
+    k.scale_only = (p.alpha == 0.0f);
+    k.aal = p.A.align_ptr; k.bal = p.B.align_ptr;
+    k.aalr = p.A.align_rs; k.aalc = p.A.align_cs; k.balr = p.B.align_rs; k.balc = p.B.align_cs;
+    k.cus = d.cus;
+    static std::mutex mu;
+    static std::unordered_map<Key, Plan, KeyHash> cache;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        auto it = cache.find(k);
+        if (it != cache.end()) return it->second;
+    }
+    Plan pl = select_plan(p, d);
+    std::lock_guard<std::mutex> g(mu);
+    auto ins = cache.emplace(k, pl);
+    if (ins.second && overrides().log) std::fprintf(stderr, "[dg] %s\n", describe(p, pl, d).c_str());
+    return ins.first->second;
+}
+
+std::string describe(const Problem &p, const Plan &pl, const Device &d) {
+    static const char *kinds[] = {"f16", "bf16", "f8e4m3"};
+    static const char *outs[] = {"f32", "f16", "bf16"};
+    static const char *modes[] = {"KMAJ", "MNMAJ"};
+    char buf[1024];
+    int n = 0;
+    auto add = [&](const char *fmt, auto... args) {
+        if (n < (int)sizeof buf) n += std::snprintf(buf + n, sizeof buf - n, fmt, args...);
+    };
+    add("M=%lld N=%lld K=%lld in=%s out=%s alpha=%g beta=%g", (long long)p.M, (long long)p.N,
+        (long long)p.K, kinds[p.in_kind], outs[p.out_kind], (double)p.alpha, (double)p.beta);
+    switch (pl.path) {
+    case Path::Noop: add(" path=noop"); break;
+    case Path::Scale: add(" path=scale"); break;
+    case Path::Skinny:
+        add(" path=skinny kind=%s mmax=%d grid=%dx%d k_per_split=%d splits=%d a_vec=%d lds=%d",
+            pl.sk_kind == SK_BN ? "BN" : "BK", pl.sk_mmax, pl.sk_grid_x, pl.splits, pl.sk_k_per_split,
+            pl.splits, pl.sk_a_vec, pl.lds_bytes);
+        break;
+    case Path::Mfma:
+        add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d tiles=%dx%d ktiles=%d splits=%d "
+            "kt_per_split=%d group_m=%d grid=%dx1x%d lds=%d",
+            mfma_tile_bm(pl.slow ? T64x64 : pl.tile), mfma_tile_bn(pl.slow ? T64x64 : pl.tile),
+            modes[pl.a.mode], modes[pl.b.mode], (int)pl.a.vec, (int)pl.b.vec, pl.slow, pl.tiles_m,
+            pl.tiles_n, pl.ktiles, pl.splits, pl.kt_per_split, pl.group_m, pl.tiles_m * pl.tiles_n,
+            pl.splits, pl.lds_bytes);
+        break;
+    }
+    add(" ws=%zu", pl.ws_bytes);
+    add(" | A %lldx%lld rs=%lld cs=%lld | B %lldx%lld rs=%lld cs=%lld | C %lldx%lld rs=%lld cs=%lld",
+        (long long)p.A.rows, (long long)p.A.cols, (long long)p.A.rs, (long long)p.A.cs,
+        (long long)p.B.rows, (long long)p.B.cols, (long long)p.B.rs, (long long)p.B.cs,
+        (long long)p.C.rows, (long long)p.C.cols, (long long)p.C.rs, (long long)p.C.cs);
+    add(" | device %s cus=%d", d.arch, d.cus);
+    return std::string(buf, std::min<size_t>(n, sizeof buf - 1));
+}
+
+}  // namespace dg

@@ -1,0 +1,73 @@
+// plan.hpp -- per-shape path and tile selection (host only, no HIP calls).
+//
+// The selection is shape-, precision- and layout-aware rather than a fixed
+// dispatch tree ("DeepGEMM is not a new model" article, cf-1.com, section 2;
+// sheratonhq.com deep dive, sections 3.1 and 5.3): thin problems (M <= 8) take
+// the streaming kernel; otherwise the matrix-core kernel with the largest
+// macro tile that still gives every CU a workgroup, and split-K when even the
+// smallest tile leaves CUs idle (sheratonhq.com deep dive, section 5.2).
+// Plans are cached per problem key under a mutex (the kwkr.cn article's
+// troubleshooting table, section 5.1, asks for thread-safe kernel caching).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "kernels.hpp"
+#include "view.hpp"
+
+namespace dg {
+
+struct Device {
+    bool present = false;     // false: planning for the default description below
+    bool gfx950 = true;
+    int cus = 256;            // compute units
+    int lds_bytes = 160 * 1024;
+    char arch[64] = "gfx950 (assumed, no device)";
+};
+
+struct Problem {
+    bool fp8 = false;
+    int in_kind = IN_BF16;
+    int out_kind = OUT_F32;
+    Mat A, B, C, SA, SB;
+    int64_t M = 0, N = 0, K = 0;
+    float alpha = 1.f, beta = 0.f;
+};
+
+enum class Path : int { Noop = 0, Scale = 1, Skinny = 2, Mfma = 3 };
+
+struct OperandPlan {
+    int mode = KMAJ;          // OpMode
+    int64_t r_stride = 0;     // bytes per row step (M for A, N for B)
+    int64_t k_stride = 0;     // bytes per K step
+    bool vec = false;         // whole 16-byte chunks are legal
+};
+
+struct Plan {
+    Path path = Path::Noop;
+    // matrix-core path
+    int tile = T256x256;
+    OperandPlan a, b;
+    int slow = 0;
+    int tiles_m = 0, tiles_n = 0, ktiles = 0, kt_per_split = 0, group_m = 1;
+    // streaming path
+    int sk_kind = SK_BN, sk_mmax = 1, sk_grid_x = 0, sk_k_per_split = 0, sk_a_vec = 0;
+    // both
+    int splits = 1;
+    size_t ws_bytes = 0;
+    int lds_bytes = 0;
+};
+
+// Choose the plan for a validated problem.  Honors DG_FORCE_PATH=skinny|mfma,
+// DG_FORCE_SPLITK=<n>, DG_FORCE_TILE=<256x256|128x128|64x64|128x64> and
+// DG_NO_VEC=1 (element-wise loads everywhere), read once per process.
+Plan select_plan(const Problem &p, const Device &d);
+
+// Same as select_plan, through a mutex-guarded cache keyed by everything the
+// selection reads.  DG_LOG=1 prints each newly cached plan to stderr.
+Plan cached_plan(const Problem &p, const Device &d);
+
+std::string describe(const Problem &p, const Plan &pl, const Device &d);
+
+}  // namespace dg

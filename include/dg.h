@@ -1,0 +1,142 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * Computes  C <- alpha * A * B + beta * C  for FP16/BF16 inputs with FP32
+ * accumulation, and an FP8 E4M3 variant whose per-token and per-block FP32
+ * scale factors are applied inside the kernel.
+ *
+ * Sources (pages cited by title and section):
+ *  - The operation, C = alpha*op(A)*op(B) + beta*C with op() folded into
+ *    strides: DeepGEMM view-native GEMM article (kwkr.cn), sections 2.3 and
+ *    4.1; "DeepGEMM: GEMM micro-kernel modelling and generation methodology for
+ *    heterogeneous chips" (xdnf.cn), section 3.1; "DeepGEMM deep dive: from
+ *    GEMM fundamentals to Tensor Core performance" (sheratonhq.com), section 1.1.
+ *  - Operands as views {ptr, shape[<=4], byte stride[<=4], dtype}: kwkr.cn
+ *    article, sections 2.1 and 3.2 (strides are bytes, not elements).
+ *  - FP8 with scale factors applied in the kernel: sheratonhq.com deep dive,
+ *    section 2.4.
+ *
+ * Conventions shared by every entry point
+ *  - Views are borrowed for the duration of the call only; the caller owns all
+ *    memory.  `ptr` is a device pointer (any HIP device allocation, e.g. a
+ *    PyTorch tensor's data_ptr()).  Buffers must stay valid until `stream`
+ *    has executed the launched work.
+ *  - A view's logical matrix: rows = row-major flattening of dims 0..ndim-2,
+ *    cols = dim ndim-1 (ndim == 1 is a single row).  Leading dims must merge
+ *    into one row stride (stride[i] == stride[i+1] * shape[i+1]) once size-1
+ *    dims are dropped; otherwise DG_ERR_UNSUPPORTED_VIEW.
+ *  - A is M x K, B is K x N, C is M x N.  Any strides >= 0 (transposes are
+ *    just strides); input views may use stride 0 (broadcast).  C must not use
+ *    stride 0 on an extent > 1 and must not overlap itself.
+ *  - alpha and beta are FP32 and must be finite.  beta == 0: C is not read
+ *    (NaN garbage in C is ignored).  alpha == 0 or K == 0: A and B are not
+ *    read and C <- beta * C.  M == 0 or N == 0: nothing happens.
+ *  - NaN/Inf in the data propagate per IEEE; nothing on the hot path checks.
+ *  - Work is enqueued on `stream` (0 = null stream) and the call returns
+ *    without synchronizing.  Launch errors are reported as DG_ERR_HIP; faults
+ *    during execution surface at the caller's next synchronization.
+ *  - On any error return, C has not been touched and nothing was enqueued.
+ *  - Thread safety: every entry point may be called concurrently from several
+ *    host threads and on several streams.  Split-K scratch memory is taken
+ *    stream-ordered (hipMallocAsync/hipFreeAsync on `stream`).
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+    DG_F32 = 0,
+    DG_F16 = 1,     /* IEEE binary16 */
+    DG_BF16 = 2,    /* bfloat16 */
+    DG_F8E4M3 = 3   /* OCP E4M3FN: bias 7, 3 mantissa bits, max 448, no Inf */
+} dg_dtype;
+
+typedef enum {
+    DG_SUCCESS = 0,
+    DG_ERR_NULL = 1,              /* null view, or null ptr with nonzero extent */
+    DG_ERR_NDIM = 2,              /* ndim outside 1..4 */
+    DG_ERR_STRIDE = 3,            /* negative stride, stride not a multiple of the element
+                                     size, negative extent, or C that overlaps itself
+                                     (e.g. stride 0 on an extent > 1) */
+    DG_ERR_SHAPE_MISMATCH = 4,    /* K, M or N disagree; scale views of the wrong shape */
+    DG_ERR_DTYPE = 5,             /* unsupported dtype or dtype combination */
+    DG_ERR_MISALIGNED = 6,        /* ptr not aligned to the element size */
+    DG_ERR_ALIAS = 7,             /* C's byte span overlaps A, B or a scale view */
+    DG_ERR_NONFINITE_SCALAR = 8,  /* alpha or beta is NaN or Inf */
+    DG_ERR_OVERFLOW = 9,          /* an extent or byte offset overflows 64 bits */
+    DG_ERR_UNSUPPORTED_VIEW = 10, /* leading dims do not merge into one row stride */
+    DG_ERR_POINTER = 11,          /* not a device pointer (checked only if DG_CHECK_POINTERS=1) */
+    DG_ERR_ARCH = 12,             /* current device is not gfx950 */
+    DG_ERR_HIP = 13,              /* a HIP runtime call or kernel launch failed */
+    DG_ERR_INVALID_ARG = 14       /* other invalid argument (e.g. a null output buffer) */
+} dg_status;
+
+/* A tensor view: up to 4 dims, strides in BYTES (kwkr.cn article, section 3.2). */
+typedef struct {
+    void *ptr;           /* address of element (0,...,0) */
+    int32_t ndim;        /* 1..4 */
+    int64_t shape[4];    /* extents; entries >= ndim are ignored */
+    int64_t stride[4];   /* byte strides; entries >= ndim are ignored */
+    dg_dtype dtype;
+} dg_view;
+
+/*
+ * C <- alpha * A * B + beta * C, FP32 accumulation.
+ *   A: M x K, B: K x N, both DG_F16 or both DG_BF16.
+ *   C: M x N, DG_F32, DG_F16 or DG_BF16; results are rounded to nearest even.
+ * Definition: kwkr.cn article, sections 2.3 and 4.1; xdnf.cn methodology, 3.1.
+ */
+dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C,
+                  float alpha, float beta, hipStream_t stream);
+
+/*
+ * FP8 E4M3 GEMM with block scales applied in the kernel:
+ *   C[m,n] <- alpha * sum_k (qA[m,k] * sA[m, k/128]) * (qB[k,n] * sB[k/128, n/128])
+ *             + beta * C[m,n]
+ *   A (qA): M x K DG_F8E4M3;  A_scale (sA): M x ceil(K/128) DG_F32 (per token,
+ *   one scale per row and 128-wide K block);  B (qB): K x N DG_F8E4M3;
+ *   B_scale (sB): ceil(K/128) x ceil(N/128) DG_F32 (one scale per 128 x 128
+ *   block).  Scale views take any strides.  C: DG_BF16, DG_F32 or DG_F16.
+ * Each K block of 128 is summed on the matrix cores and promoted into the FP32
+ * accumulator with its scale product exactly once (sheratonhq.com deep dive,
+ * sections 2.4 and 4.2).
+ */
+dg_status dg_gemm_fp8(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                      const dg_view *B_scale, const dg_view *C, float alpha, float beta,
+                      hipStream_t stream);
+
+/*
+ * Validate the arguments of dg_gemm exactly as dg_gemm does and write a
+ * one-line, NUL-terminated description of the chosen plan (path, tiles,
+ * split-K, grid, canonical operand layouts) into buf[0..len-1], without
+ * launching anything.  Needs no GPU: with no device visible it plans for a
+ * 256-CU gfx950.  Returns the status dg_gemm would return before launching.
+ * buf may be NULL only if len == 0.
+ */
+dg_status dg_gemm_plan(const dg_view *A, const dg_view *B, const dg_view *C,
+                       float alpha, float beta, char *buf, size_t len);
+
+/* Same as dg_gemm_plan for the arguments of dg_gemm_fp8. */
+dg_status dg_gemm_fp8_plan(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                           const dg_view *B_scale, const dg_view *C, float alpha, float beta,
+                           char *buf, size_t len);
+
+/* Static, human-readable name of a status code ("DG_ERR_ALIAS", ...). */
+const char *dg_status_str(dg_status s);
+
+/* DG_VERSION of the built library. */
+int dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -181,4 +181,4 @@ def num_threads() -> int:
     return lib().or_num_threads()
 
 
-from .compare import bound, compare, CompareReport, ulp  # noqa: E402,F401
+from .compare import bound, compare, CompareReport, ulp, fmt_of  # noqa: E402,F401
