@@ -1,0 +1,319 @@
+"""Benchmark of the gfx950 dense GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs all|none|c1,c4,...]
+                    [--no-cpu] [--copy-calib]
+
+One step is one pass of the thin-GEMM workload the pages single out: the BF16
+x.W1 up-projection of an MoE FFN, [1,4096] x [4096,14336], followed by the
+query x 128-key cache product [1,4096] x [4096,128] (B = K_cache^T).  Both run
+through the C ABI (view parse, plan, skinny streaming kernel, epilogue), with
+every input already resident in HBM: W1 and the cache are rotated over enough
+distinct copies (>= 1 GiB in all) that neither the 256 MB Infinity Cache nor
+the L2 can serve a repeat.  `value` is the step's algorithmic bytes (each
+operand read once, C written once) per second.
+
+The JSON line also carries:
+  roofline      the x.W1 kernel's achieved HBM rate (its algorithmic bytes over
+                its average duration, timed with HIP events on the launch stream
+                inside the timed region) against the 8 TB/s HBM3E peak, and the
+                HBM traffic read from rocprofv3 counters (profiles/), or null when
+                the kernel source changed since they were taken;
+  cpu_baseline  the FP64 CPU oracle on the same step, on the host's cores;
+  configs       every other workload shape timed the same way (TFLOPS and the
+                fraction of the dense MFMA peak for M >= 64, GB/s and the
+                fraction of HBM peak for the thin and HBM-bound shapes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2}   # dense TFLOP/s
+CACHE_DEFEAT_BYTES = 1 << 30   # rotate buffer sets until this many bytes are distinct
+DOMINANT_KERNEL = "skinny_bn"  # the kernel that moves the x.W1 bytes
+KERNEL_SOURCES = ["dense_gemm_19_amd/csrc/skinny.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "skinny_bn_c2a_traffic.txt")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- workload bytes and flops
+
+def algorithmic(case):
+    """(bytes, flops) of one GEMM: each operand read once, C written once (and
+    read once more when beta != 0), plus the FP8 scale tensors."""
+    import math
+    M, N, K = case.mnk
+    es = lambda t: t.element_size()
+    b = M * K * es(case.A) + K * N * es(case.B) + M * N * es(case.C) * (2 if case.beta != 0 else 1)
+    if case.fp8:
+        b += 4 * (M * math.ceil(K / 128) + math.ceil(K / 128) * math.ceil(N / 128))
+    return b, 2.0 * M * N * K
+
+
+def storage_bytes(case):
+    tot = 0
+    for t in (case.A, case.B, case.C, case.A_scale, case.B_scale):
+        if t is not None:
+            tot += t.untyped_storage().nbytes()
+    return tot
+
+
+# ---------------------------------------------------------------- device buffer sets
+
+def clone_view(t):
+    """A copy of t's whole storage at a new address, viewed with t's geometry."""
+    import torch
+    if t is None:
+        return None
+    raw = torch.empty(0, dtype=torch.uint8, device=t.device).set_(t.untyped_storage())
+    dup = raw.clone()
+    return torch.empty(0, dtype=t.dtype, device=t.device).set_(
+        dup.untyped_storage(), t.storage_offset(), t.shape, t.stride())
+
+
+def rotated_sets(case, device, min_bytes=CACHE_DEFEAT_BYTES, max_sets=4096):
+    import synth
+    d0 = case.to(device)
+    per = storage_bytes(d0)
+    P = max(2, min(max_sets, -(-min_bytes // max(per, 1))))
+    sets = [d0]
+    for _ in range(P - 1):
+        sets.append(synth.Case(d0.name, clone_view(d0.A), clone_view(d0.B), clone_view(d0.C),
+                               d0.alpha, d0.beta, clone_view(d0.A_scale), clone_view(d0.B_scale),
+                               d0.rtol))
+    return sets
+
+
+def launch(dg, c):
+    if c.fp8:
+        dg.gemm_fp8(c.A, c.A_scale, c.B, c.B_scale, c.C, c.alpha, c.beta)
+    else:
+        dg.gemm(c.A, c.B, c.C, c.alpha, c.beta)
+
+
+# ---------------------------------------------------------------- timing
+
+def time_config(dg, name, reps=None, trials=5):
+    """Per-launch time of one workload over rotated buffer sets (median of trials)."""
+    import torch
+    import synth
+    case = synth.config(name)
+    sets = rotated_sets(case, "cuda:0")
+    nbytes, flops = algorithmic(case)
+    if reps is None:   # aim for a few ms per trial
+        reps = max(20, min(2000, int(2e-3 / max(flops / 2e15, nbytes / 6e12, 2e-6))))
+    for i in range(10):
+        launch(dg, sets[i % len(sets)])
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            launch(dg, sets[i % len(sets)])
+        e1.record()
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    per.sort()
+    t = per[len(per) // 2]
+    M = case.mnk[0]
+    plan = dg.plan(sets[0].A, sets[0].B, sets[0].C, case.alpha, case.beta, sets[0].A_scale,
+                   sets[0].B_scale)
+    dt = "fp8" if case.fp8 else ("bf16" if case.A.dtype == torch.bfloat16 else "f16")
+    tflops = flops / t / 1e12
+    gbs = nbytes / t / 1e9
+    rec = {"us": round(t * 1e6, 3), "us_min": round(per[0] * 1e6, 3), "reps": reps,
+           "buffer_sets": len(sets), "tflops": round(tflops, 2),
+           "frac_mfma_peak": round(tflops / MFMA_PEAK[dt], 4), "gbs": round(gbs, 1),
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "dtype": dt, "mnk": list(case.mnk),
+           "path": re.search(r"path=(\S+)", plan).group(1)}
+    m = re.search(r"tile=(\S+)", plan)
+    if m:
+        rec["tile"] = m.group(1)
+    m = re.search(r"splits=(\d+)", plan)
+    if m:
+        rec["splits"] = int(m.group(1))
+    del sets
+    torch.cuda.empty_cache()
+    return rec
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES + ["dense_gemm_19_amd/csrc/device_common.hpp",
+                               "dense_gemm_19_amd/csrc/kernels.hpp"]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(launch_bytes):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if it is missing or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    m_t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_t or m_hash.group(1) != source_hash():
+        return None
+    return float(m_t.group(1))
+
+
+def cpu_baseline(cases, budget_s=12.0):
+    """The FP64 oracle on whole steps, repeated until about budget_s of CPU work."""
+    import oracle
+    nbytes = sum(algorithmic(c)[0] for c in cases)
+    views = [(oracle.host_view(c.A), oracle.host_view(c.B)) for c in cases]
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 400:
+        t0 = time.perf_counter()
+        for c, (a, b) in zip(cases, views):
+            oracle.ref_gemm(a, b, None, c.alpha, 0.0)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(nbytes * reps / t_total / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} whole steps (x.W1 1x4096x14336 + q.K_cache^T 1x4096x128, BF16 in, "
+                      f"FP64 arithmetic) in {t_total:.1f} s"}
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes read, {nbytes} bytes written")
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--configs", default="all",
+                    help="other workloads to time: all, none, or a comma list of c1,c3,c4,c5_128,c5_4096")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import dense_gemm_19_amd as dg
+    dg.lib()   # raises if the HIP library is missing: there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+
+    # ---- the step: x.W1 then q.K_cache^T, rotated over >= 1 GiB of distinct buffers
+    c2a, c2b = synth.config("c2a"), synth.config("c2b")
+    sa_sets = rotated_sets(c2a, dev)
+    sb_sets = rotated_sets(c2b, dev)
+    P = max(len(sa_sets), len(sb_sets))
+    bytes_a, _ = algorithmic(c2a)
+    bytes_b, _ = algorithmic(c2b)
+    step_bytes = bytes_a + bytes_b
+    log(f"step: x.W1 {c2a.mnk} + q.Kc {c2b.mnk}; {step_bytes} algorithmic bytes; "
+        f"{len(sa_sets)} / {len(sb_sets)} rotated buffer sets")
+    log("plan x.W1:", dg.plan(sa_sets[0].A, sa_sets[0].B, sa_sets[0].C))
+    log("plan q.Kc:", dg.plan(sb_sets[0].A, sb_sets[0].B, sb_sets[0].C))
+
+    def step(i, ev=None):
+        a = sa_sets[i % len(sa_sets)]
+        if ev is not None:
+            ev[0].record()
+        dg.gemm(a.A, a.B, a.C)
+        if ev is not None:
+            ev[1].record()
+        b = sb_sets[i % len(sb_sets)]
+        dg.gemm(b.A, b.B, b.C)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # events around every x.W1 launch, on the stream the library launches on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    k_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    k_avg = sum(k_ms) / len(k_ms)
+    achieved = bytes_a / (k_avg * 1e-3) / 1e9
+    log(f"{args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s; "
+        f"x.W1 launch avg {k_avg * 1e3:.2f} us (median {k_ms[len(k_ms) // 2] * 1e3:.2f}) "
+        f"-> {achieved:.1f} GB/s")
+    traffic = traffic_from_profiles(bytes_a)
+    del sa_sets, sb_sets
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads
+    others = {}
+    names = [] if args.configs == "none" else (
+        ["c1", "c3", "c4", "c5_128", "c5_4096"] if args.configs == "all" else args.configs.split(","))
+    for n in names:
+        others[n] = time_config(dg, n)
+        log(n, json.dumps(others[n]))
+
+    if args.copy_calib:
+        copy_calibration()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline([c2a, c2b])
+        log("cpu baseline:", json.dumps(cpu))
+
+    out = {
+        "metric": "GB/s & % HBM peak (M=1 thin GEMM); TFLOPS & % MFMA peak (M>=64) in configs",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "thin BF16 GEMM: x[1,4096] . W1[4096,14336] (row-major W1) + "
+                               "q[1,4096] . K_cache[128,4096]^T, FP32 accumulate, BF16 C",
+                   "M": 1, "K": 4096, "N": [14336, 128], "buffer_sets": P,
+                   "inputs": "N(0,1) seeded, resident in HBM, rotated over >= 1 GiB",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": bytes_a,
+                     "avg_launch_us": round(k_avg * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "configs": others,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
