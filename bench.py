@@ -96,11 +96,37 @@ def rotated_sets(case, device, min_bytes=CACHE_DEFEAT_BYTES, max_sets=4096):
     return sets
 
 
-def launch(dg, c):
-    if c.fp8:
-        dg.gemm_fp8(c.A, c.A_scale, c.B, c.B_scale, c.C, c.alpha, c.beta)
-    else:
-        dg.gemm(c.A, c.B, c.C, c.alpha, c.beta)
+class Call:
+    """One prepared C-ABI call: the dg_view structs are built once, so the timed
+    loop pays only for the ctypes call itself (the library still validates,
+    plans and launches on every call)."""
+
+    def __init__(self, dg, c, stream):
+        import ctypes
+        self.views = [dg.view_of(t) for t in ((c.A, c.A_scale, c.B, c.B_scale, c.C) if c.fp8
+                                              else (c.A, c.B, c.C))]
+        self.args = [ctypes.byref(v) for v in self.views] + [c.alpha, c.beta, stream]
+        self.fn = dg.lib().dg_gemm_fp8 if c.fp8 else dg.lib().dg_gemm
+        self.name = "dg_gemm_fp8" if c.fp8 else "dg_gemm"
+
+    def __call__(self):
+        return self.fn(*self.args)
+
+
+def prepared(dg, sets):
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    return [Call(dg, c, stream) for c in sets]
+
+
+def run_checked(calls, idx):
+    """Launch calls[i % len] for i in idx; raise on the first non-zero status."""
+    n = len(calls)
+    bad = 0
+    for i in idx:
+        bad |= calls[i % n]()
+    if bad:
+        raise RuntimeError(f"{calls[0].name} returned an error status in the timed loop")
 
 
 # ---------------------------------------------------------------- timing
@@ -111,19 +137,18 @@ def time_config(dg, name, reps=None, trials=5):
     import synth
     case = synth.config(name)
     sets = rotated_sets(case, "cuda:0")
+    calls = prepared(dg, sets)
     nbytes, flops = algorithmic(case)
     if reps is None:   # aim for a few ms per trial
         reps = max(20, min(2000, int(2e-3 / max(flops / 2e15, nbytes / 6e12, 2e-6))))
-    for i in range(10):
-        launch(dg, sets[i % len(sets)])
+    run_checked(calls, range(10))
     torch.cuda.synchronize()
     per = []
     for _ in range(trials):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(reps):
-            launch(dg, sets[i % len(sets)])
+        run_checked(calls, range(reps))
         e1.record()
         e1.synchronize()
         per.append(e0.elapsed_time(e1) * 1e-3 / reps)
@@ -242,33 +267,40 @@ def main():
     log("plan x.W1:", dg.plan(sa_sets[0].A, sa_sets[0].B, sa_sets[0].C))
     log("plan q.Kc:", dg.plan(sb_sets[0].A, sb_sets[0].B, sb_sets[0].C))
 
-    def step(i, ev=None):
-        a = sa_sets[i % len(sa_sets)]
-        if ev is not None:
-            ev[0].record()
-        dg.gemm(a.A, a.B, a.C)
-        if ev is not None:
-            ev[1].record()
-        b = sb_sets[i % len(sb_sets)]
-        dg.gemm(b.A, b.B, b.C)
+    calls_a, calls_b = prepared(dg, sa_sets), prepared(dg, sb_sets)
+    na, nb = len(calls_a), len(calls_b)
 
-    for i in range(args.warmup):
-        step(i)
+    def steps(lo, hi):
+        bad = 0
+        for i in range(lo, hi):
+            bad |= calls_a[i % na]()
+            bad |= calls_b[i % nb]()
+        if bad:
+            raise RuntimeError("dg_gemm returned an error status in the timed loop")
+
+    steps(0, args.warmup)
     torch.cuda.synchronize()
-    # events around every x.W1 launch, on the stream the library launches on
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region 1: K whole steps back to back on the current stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
+    steps(args.warmup, args.warmup + args.steps)
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # timed region 2: the x.W1 launch alone, a HIP event pair around each launch
+    # on the stream the library launches on, giving its average duration
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        st = calls_a[i % na]()
+        e1.record()
+        if st:
+            raise RuntimeError("dg_gemm returned an error status")
+    torch.cuda.synchronize()
     k_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     k_avg = sum(k_ms) / len(k_ms)
     achieved = bytes_a / (k_avg * 1e-3) / 1e9

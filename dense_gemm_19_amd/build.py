@@ -1,6 +1,6 @@
 """Build libdg.so for gfx950 with hipcc (every source, every call).
 
-    python -m dense_gemm_19_amd.build
+    python -m dense_gemm_19_amd.build [-v] [--incremental]
 
 Objects go to dense_gemm_19_amd/_build/; the library to dense_gemm_19_amd/libdg.so.
 """
@@ -28,8 +28,18 @@ HIP_SOURCES = ["gemm_mfma.hip", "skinny.hip", "epilogue.hip"]
 HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp"]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _newest_header() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
+    hs.append(os.path.join(ROOT, "include", "dg.h"))
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        t = os.path.getmtime(obj)
+        if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
+            return obj
     flags = HIP_FLAGS if src.endswith(".hip") else HOST_FLAGS
     cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
@@ -44,12 +54,14 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every source (or, with incremental=True, those newer than their
+    object) and link libdg.so."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = HIP_SOURCES + HOST_SOURCES
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -60,4 +72,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -6,6 +6,7 @@
 // offsets, NaN/Inf alpha/beta, device pointers, thread-safe kernel caching).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -123,6 +124,66 @@ dg_status current_device(Device *d, bool require) {
     return DG_SUCCESS;
 }
 
+// Split-K scratch: per (device, stream), an FP32 partial-sum buffer and a block
+// of arrival counters, grown on demand and kept for the life of the process.
+// Work on one stream runs in order, so a stream's buffers are never used by two
+// launches at once; different streams never share them.  Counters are zeroed
+// (on the stream) when allocated, and every kernel that uses them leaves them
+// at zero.  Growing waits for the stream, since the old buffer may be in use.
+struct Workspace {
+    std::mutex mu;
+    struct Entry { int dev; hipStream_t stream; void *ptr; size_t bytes; int *cnt; size_t ncnt; };
+    Entry e[64];
+    int n = 0;
+};
+
+Workspace &workspace() {
+    static Workspace w;
+    return w;
+}
+
+hipError_t release(Workspace::Entry &x) {
+    hipError_t err = hipSuccess;
+    if (x.ptr || x.cnt) err = hipStreamSynchronize(x.stream);
+    if (err == hipSuccess && x.ptr) err = hipFree(x.ptr);
+    if (err == hipSuccess && x.cnt) err = hipFree(x.cnt);
+    x.ptr = nullptr; x.bytes = 0; x.cnt = nullptr; x.ncnt = 0;
+    return err;
+}
+
+hipError_t get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, float **ws, int **counters) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    Workspace &w = workspace();
+    std::lock_guard<std::mutex> g(w.mu);
+    Workspace::Entry *slot = nullptr;
+    for (int i = 0; i < w.n; ++i)
+        if (w.e[i].dev == dev && w.e[i].stream == stream) slot = &w.e[i];
+    if (!slot) {
+        if (w.n == 64) {   // table full: recycle the oldest entry after its stream drains
+            if ((err = release(w.e[0])) != hipSuccess) return err;
+            for (int i = 1; i < w.n; ++i) w.e[i - 1] = w.e[i];
+            --w.n;
+        }
+        slot = &w.e[w.n++];
+        *slot = Workspace::Entry{dev, stream, nullptr, 0, nullptr, 0};
+    }
+    if (slot->bytes < bytes || slot->ncnt < ncounters) {
+        const size_t want_b = std::max<size_t>({bytes, slot->bytes, 1 << 20});
+        const size_t want_c = std::max<size_t>({ncounters, slot->ncnt, 4096});
+        if ((err = release(*slot)) != hipSuccess) return err;
+        if ((err = hipMalloc(&slot->ptr, want_b)) != hipSuccess) return err;
+        slot->bytes = want_b;
+        if ((err = hipMalloc(reinterpret_cast<void **>(&slot->cnt), want_c * sizeof(int))) != hipSuccess) return err;
+        slot->ncnt = want_c;
+        if ((err = hipMemsetAsync(slot->cnt, 0, want_c * sizeof(int), stream)) != hipSuccess) return err;
+    }
+    *ws = static_cast<float *>(slot->ptr);
+    *counters = slot->cnt;
+    return hipSuccess;
+}
+
 dg_status check_pointer(const void *p) {
     if (!p) return DG_SUCCESS;
     hipPointerAttribute_t attr;
@@ -154,11 +215,10 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         return launch_scale(s, stream) == hipSuccess ? DG_SUCCESS : DG_ERR_HIP;
     }
     float *ws = nullptr;
-    if (pl.splits > 1) {
-        if (hipMallocAsync(reinterpret_cast<void **>(&ws), pl.ws_bytes, stream) != hipSuccess) {
-            (void)hipGetLastError();
-            return DG_ERR_HIP;
-        }
+    int *counters = nullptr;
+    if (pl.splits > 1 && get_workspace(stream, pl.ws_bytes, (size_t)pl.counters, &ws, &counters) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
     }
     hipError_t e;
     if (pl.path == Path::Skinny) {
@@ -167,12 +227,14 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         a.B = p.B.ptr; a.b_rs = p.B.rs; a.b_cs = p.B.cs;
         a.epi = epi;
         a.ws = ws;
+        a.counters = counters;
         a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
         a.in_kind = p.in_kind;
         a.a_vec = pl.sk_a_vec;
         a.splits = pl.splits;
         a.k_per_split = pl.sk_k_per_split;
-        e = launch_skinny(pl.sk_kind, pl.sk_mmax, a, pl.sk_grid_x, stream);
+        a.kc = pl.sk_kc;
+        e = launch_skinny(pl.sk_kind, pl.sk_mmax, a, pl.sk_grid_x, pl.sk_waves, stream);
     } else {
         MfmaArgs a;
         a.a = Operand{p.A.ptr, pl.a.r_stride, pl.a.k_stride, pl.a.vec ? 1 : 0};
@@ -191,12 +253,12 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         a.group_m = pl.group_m;
         e = launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
     }
-    if (e == hipSuccess && pl.splits > 1) {
+    // split-K partials are summed by a second kernel, except where the streaming
+    // kernel sums them itself (its last workgroup per column slab)
+    const bool fused = pl.path == Path::Skinny && pl.sk_kind == SK_BN;
+    if (e == hipSuccess && pl.splits > 1 && !fused) {
         ReduceArgs r{ws, epi, (int)p.M, (int)p.N, pl.splits};
         e = launch_reduce(r, stream);
-    }
-    if (ws) {
-        if (hipFreeAsync(ws, stream) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     }
     if (e != hipSuccess) {
         (void)hipGetLastError();

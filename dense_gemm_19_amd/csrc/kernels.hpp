@@ -55,12 +55,27 @@ struct SkinnyArgs {
     const char *B; int64_t b_rs, b_cs;   // K x N
     Epilogue epi;
     float *ws;                            // [S][M][N] partials when S > 1
+    int *counters;                        // SK_BN, S > 1: one per column slab, 0 on entry and exit
     int M, N, K;
     int in_kind;                          // IN_F16 / IN_BF16
     int a_vec;                            // SK_BK: A rows K-contiguous and 16-byte aligned
     int splits;                           // S
     int k_per_split;                      // rows of K per split (multiple of 8)
+    int kc;                               // SK_BN: rows of A staged in LDS at a time
 };
+
+// SK_BN geometry: 512 threads, 256 columns per workgroup, 128-row sweeps; the
+// A chunk kc is a multiple of the sweep.
+constexpr int SKINNY_BN_THREADS = 512;
+constexpr int SKINNY_BN_COLS = 256;
+constexpr int SKINNY_BN_SWEEP = 128;
+// LDS bytes of SK_BN: the A chunk [mmax][kc] 16-bit plus a spare 16-byte slot,
+// or the cross-wave reduction buffer [8 waves][mmax][256] FP32, whichever is
+// larger.
+inline int skinny_bn_lds(int mmax, int kc) {
+    const int a = mmax * kc * 2 + 16, r = (SKINNY_BN_THREADS / 64) * mmax * SKINNY_BN_COLS * 4;
+    return a > r ? a : r;
+}
 
 struct ReduceArgs {
     const float *ws;    // [S][M][N]
@@ -88,7 +103,9 @@ enum SkinnyKind : int { SK_BN = 0 /* B N-contiguous */, SK_BK = 1 /* B K-contigu
 // slow != 0 selects the element-wise loader (any strides, any K) on a 64x64 tile.
 hipError_t launch_mfma(int in_kind, int tile, int a_mode, int b_mode, int slow,
                        const MfmaArgs &args, hipStream_t stream);
-hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, hipStream_t stream);
+// waves: SK_BK waves (columns) per workgroup; ignored by SK_BN.
+hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
+                         hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);
 

@@ -77,29 +77,35 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
     const Mat &A = p.A, &B = p.B;
     const int mmax = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
     const bool no_vec = overrides().no_vec;
-    // B N-contiguous: stream rows of B with 16-byte loads.
+    // B N-contiguous: stream 512-byte row pieces of B, 256 columns per workgroup.
     if (!no_vec && B.cols_contig() && B.cs == B.esize && B.align_ptr >= 16 && (p.K <= 1 || B.align_rs >= 16)) {
         pl.sk_kind = SK_BN;
-        pl.sk_grid_x = (int)cdiv(p.N, 64);
-        const int64_t kmax_lds = 8192 / mmax;            // A slice <= 32 KB of LDS
-        int64_t S = cdiv(4LL * d.cus, pl.sk_grid_x);
-        S = std::min<int64_t>(S, std::max<int64_t>(1, p.K / 256));
-        S = std::max<int64_t>(S, cdiv(p.K, kmax_lds));
+        pl.sk_grid_x = (int)cdiv(p.N, SKINNY_BN_COLS);
+        // Split K until about two workgroups per CU stream B (the last one of a
+        // slab sums the partials), keeping at least one sweep per split.
+        int64_t S = std::max<int64_t>(1, std::min<int64_t>(cdiv(2LL * d.cus, pl.sk_grid_x),
+                                                           p.K / (2 * SKINNY_BN_SWEEP)));
         if (overrides().force_splitk > 0) S = overrides().force_splitk;
         S = std::max<int64_t>(1, std::min<int64_t>(S, std::max<int64_t>(1, p.K)));
+        // splits and LDS chunks are whole sweeps (only the last sweep of K is partial)
+        const int64_t sweep = SKINNY_BN_SWEEP;
         int64_t kps = cdiv(std::max<int64_t>(p.K, 1), S);
-        kps = cdiv(kps, 8) * 8;
-        if (kps > kmax_lds) return false;
+        kps = cdiv(kps, sweep) * sweep;
         pl.sk_k_per_split = (int)kps;
         pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
         pl.sk_mmax = mmax;
-        pl.lds_bytes = (int)std::max<int64_t>(kps * mmax * 4, 4LL * mmax * 64 * 4);
+        // A chunk in LDS: a multiple of the sweep, at most 32 KB
+        const int64_t kc_max = std::max<int64_t>(sweep, (16384 / mmax) / sweep * sweep);
+        pl.sk_kc = (int)std::min<int64_t>(cdiv(kps, sweep) * sweep, kc_max);
+        pl.lds_bytes = skinny_bn_lds(mmax, pl.sk_kc);
+        pl.counters = pl.splits > 1 ? pl.sk_grid_x : 0;
         return true;
     }
     // B K-contiguous (e.g. a transposed cache): one wave per column.
     if (!no_vec && B.rows_contig() && B.rs == B.esize && B.align_ptr >= 16 && (p.N <= 1 || B.align_cs >= 16)) {
         pl.sk_kind = SK_BK;
-        pl.sk_grid_x = (int)cdiv(p.N, 4);
+        pl.sk_waves = p.N < 1024 ? 1 : 4;   // few columns: one per workgroup, spread over CUs
+        pl.sk_grid_x = (int)cdiv(p.N, pl.sk_waves);
         int64_t S = 1;
         if (overrides().force_splitk > 0) S = overrides().force_splitk;
         int64_t kps = cdiv(cdiv(std::max<int64_t>(p.K, 1), S), 8) * 8;
@@ -234,9 +240,9 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
     case Path::Noop: add(" path=noop"); break;
     case Path::Scale: add(" path=scale"); break;
     case Path::Skinny:
-        add(" path=skinny kind=%s mmax=%d grid=%dx%d k_per_split=%d splits=%d a_vec=%d lds=%d",
+        add(" path=skinny kind=%s mmax=%d grid=%dx%d k_per_split=%d splits=%d kc=%d waves=%d a_vec=%d lds=%d",
             pl.sk_kind == SK_BN ? "BN" : "BK", pl.sk_mmax, pl.sk_grid_x, pl.splits, pl.sk_k_per_split,
-            pl.splits, pl.sk_a_vec, pl.lds_bytes);
+            pl.splits, pl.sk_kc, pl.sk_kind == SK_BN ? SKINNY_BN_THREADS / 64 : pl.sk_waves, pl.sk_a_vec, pl.lds_bytes);
         break;
     case Path::Mfma:
         add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d tiles=%dx%d ktiles=%d splits=%d "

@@ -53,9 +53,12 @@ struct Plan {
     int tiles_m = 0, tiles_n = 0, ktiles = 0, kt_per_split = 0, group_m = 1;
     // streaming path
     int sk_kind = SK_BN, sk_mmax = 1, sk_grid_x = 0, sk_k_per_split = 0, sk_a_vec = 0;
+    int sk_kc = 0;            // SK_BN: A rows staged in LDS per chunk
+    int sk_waves = 1;         // SK_BK: waves (columns) per workgroup
     // both
     int splits = 1;
     size_t ws_bytes = 0;
+    int counters = 0;         // split-K arrival counters the kernel needs (0 on entry)
     int lds_bytes = 0;
 };
 

@@ -2,36 +2,44 @@
 //
 // The pages single out thin shapes such as x[1,4096] . W1[4096,14336] (an MoE
 // FFN up-projection) and q[1,4096] . K_cache^T (a 128-key cache): with M this
-// small the work is one pass over B, so the kernel is built to stream B exactly
-// once with 16-byte loads and reduce with cross-lane shuffles instead of
-// issuing matrix-core instructions ("DeepGEMM is not a new model" article,
-// cf-1.com, sections 2 and 4; sheratonhq.com deep dive, section 5.4).  The
-// stores are plain, one writer per output element, with no atomics (cf-1.com
-// article, section 4.5).
+// small the work is one pass over B, so the kernels stream B exactly once with
+// 16-byte loads, multiply on the vector ALUs, and reduce with cross-lane
+// shuffles and LDS instead of issuing matrix-core instructions ("DeepGEMM is
+// not a new model" article, cf-1.com, sections 2 and 4; sheratonhq.com deep
+// dive, section 5.4).  Stores are plain, one writer per output element, with
+// no atomics (cf-1.com article, section 4.5), so results are reproducible.
 //
-// SK_BN: B is N-contiguous (row-major [K][N], e.g. W1).  A workgroup owns 64
-//   columns; each lane owns 8 adjacent columns (one 16-byte load per K row) and
-//   every 32nd K row of the workgroup's K slice; the 32 K groups of the
-//   workgroup are summed with cross-lane shuffles, then through LDS, always in
-//   the same order.  A's K slice is staged in LDS as [k][m] so one LDS read
-//   broadcasts A[0..M)[k] to a whole K group.
-// SK_BK: B is K-contiguous (B = K_cache^T, each column a contiguous row of the
-//   cache).  A wave owns one column; lanes stride K with 16-byte loads of B and
-//   A, and the wave reduces with shuffles.
-// With grid.y = S > 1 the K range is split and FP32 partials go to a workspace
-// that the reduction kernel sums in a fixed order.
+// SK_BN: B is N-contiguous (row-major [K][N], e.g. W1).  A workgroup of 8 waves
+//   owns a slab of 64 columns (128 bytes of every row of B) and, unless K is
+//   split, all of K.  Lane (r, c) of a wave, r = lane/8, c = lane%8, owns
+//   columns 8c..8c+7 of the slab and, in each sweep, the U consecutive rows
+//   U*(8*wave + r) + u, u < U (U = 16 for M <= 2, else 8): each of its U loads
+//   is one 16-byte piece of a row, so every load instruction of a wave covers 8
+//   full 128-byte lines, and the A values a lane needs are 16-byte LDS reads.
+//   A lane issues its U loads, then multiplies; with 4 waves per SIMD the other
+//   waves' loads are in flight meanwhile (U*16 bytes per lane, 256 KB per CU
+//   for U = 16).  A's K slice is staged in LDS as 16-bit values [m][k].  The 8
+//   row groups of a wave are summed with shuffles and the 16 waves through LDS,
+//   always in the same order.
+// SK_BK: B is K-contiguous (B = K_cache^T: column n is row n of the cache).  A
+//   wave owns one column; lanes take 8 consecutive K values each per 512-wide K
+//   step, with up to 8 steps' loads of B and A issued before any is used, then a
+//   wave reduction with shuffles.  Workgroups hold 1 wave when N is small (to
+//   spread the columns over many compute units) and 4 otherwise.
+// SK_BK with grid.y = S > 1 splits K too, and a reduction kernel sums the FP32
+// partials in a fixed order.
 #include "device_common.hpp"
 
 namespace dg {
 namespace {
 
-constexpr int NT = 256;
-
-__device__ __forceinline__ void unpack8(u32x4 v, int in_kind, float (&f)[8]) {
+// 16-byte chunk of 8 bf16/f16 values -> 8 floats.
+template <int IN>
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t w = v[q];
-        if (in_kind == IN_BF16) {
+        if (IN == IN_BF16) {
             f[2 * q] = __builtin_bit_cast(float, w << 16);
             f[2 * q + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
         } else {
@@ -41,135 +49,245 @@ __device__ __forceinline__ void unpack8(u32x4 v, int in_kind, float (&f)[8]) {
     }
 }
 
-__device__ __forceinline__ float load_in(const char *p, int in_kind) {
-    const uint16_t b = *reinterpret_cast<const uint16_t *>(p);
-    return in_kind == IN_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+template <int IN>
+__device__ __forceinline__ float to_f32(uint16_t b) {
+    return IN == IN_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
 }
 
 // ------------------------------------------------------------------ SK_BN
 
-constexpr int BN_COLS = 64;              // columns per workgroup (8 lanes x 8)
-constexpr int BN_KG = NT / 8;            // K groups per workgroup
-constexpr int BN_UNROLL = 8;             // 16-byte B loads in flight per lane
+// Global-address-space view of 16 bytes (keeps loads "global", not "flat").
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+// 16 zero bytes in device memory: the source of out-of-range row loads.
+__device__ __attribute__((aligned(16))) const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
+
+constexpr int BN_NT = SKINNY_BN_THREADS;        // 8 waves
+constexpr int BN_WAVES = BN_NT / 64;
+constexpr int BN_W = 32;                        // lanes per row: 512 contiguous bytes of a row
+constexpr int BN_R = 64 / BN_W;                 // rows per load instruction of a wave
+constexpr int BN_COLS = SKINNY_BN_COLS;         // columns per workgroup (BN_W lanes x 8)
+constexpr int BN_U = 8;                         // consecutive rows per lane per sweep
+constexpr int BN_SWEEP = BN_WAVES * BN_R * BN_U;
+static_assert(BN_COLS == BN_W * 8 && BN_SWEEP == SKINNY_BN_SWEEP, "shared with the planner");
 
 template <int MMAX, int IN>
-__global__ void __launch_bounds__(NT) skinny_bn(SkinnyArgs p) {
+__global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    // LDS: A slice as float [k_per_split][MMAX], then the reduction buffer.
-    float *la = reinterpret_cast<float *>(smem);
+    // LDS: A chunk as 16-bit values [MMAX][kc] (kc a multiple of BN_SWEEP), later
+    // reused for the cross-wave reduction red[wave][m][BN_COLS].
+    uint16_t *la = reinterpret_cast<uint16_t *>(smem);
+    float *red = reinterpret_cast<float *>(smem);
+    __shared__ int is_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tc = tid & 7;              // column group within the workgroup
-    const int kg = tid >> 3;             // K group 0..31
-    const int n0 = blockIdx.x * BN_COLS + tc * 8;
+    const int c = lane % BN_W, r = lane / BN_W;
+    const int n0 = blockIdx.x * BN_COLS + c * 8;
     const int z = blockIdx.y;
     const int kb = z * p.k_per_split;
     const int ke = min(kb + p.k_per_split, p.K);
-    const int klen = ke - kb;
-
-    // Stage A[0..M)[kb..ke) into LDS as [k][m] FP32.
-    for (int idx = tid; idx < klen * MMAX; idx += NT) {
-        const int k = idx / MMAX, m = idx - k * MMAX;
-        float v = 0.f;
-        if (m < p.M) v = load_in(p.A + (int64_t)m * p.a_rs + (int64_t)(kb + k) * p.a_cs, IN);
-        la[idx] = v;
-    }
-    __syncthreads();
+    // every column of the slab exists: the vector path (uniform over the workgroup)
+    const bool slab_full = (blockIdx.x + 1) * BN_COLS <= p.N;
+    const char *bcol = p.B + (int64_t)n0 * p.b_cs;
 
     float acc[MMAX][8];
 #pragma unroll
     for (int m = 0; m < MMAX; ++m)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[m][c] = 0.f;
+        for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
 
-    const bool full = n0 + 8 <= p.N;
-    const char *bcol = p.B + (int64_t)n0 * p.b_cs;
-    if (full) {
-        // main stream: rows kb + kg + BN_KG * t
-        int k = kg;
-        for (; k + BN_KG * (BN_UNROLL - 1) < klen; k += BN_KG * BN_UNROLL) {
-            u32x4 v[BN_UNROLL];
+    const int lrow = wave * (BN_R * BN_U) + r * BN_U;   // first of the lane's rows in a sweep
+
+    auto fma_sweep = [&](const u32x4 (&v)[BN_U], int k) {   // k: the lane's first row in the chunk
 #pragma unroll
-            for (int u = 0; u < BN_UNROLL; ++u)
-                v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    bcol + (int64_t)(kb + k + BN_KG * u) * p.b_rs));
+        for (int m = 0; m < MMAX; ++m) {
+            // A[m][k .. k+7]: one 16-byte LDS read (zero beyond the chunk end)
+            const u32x4 av = *reinterpret_cast<const u32x4 *>(la + m * p.kc + k);
+            float a[8];
+            unpack8<IN>(av, a);
 #pragma unroll
-            for (int u = 0; u < BN_UNROLL; ++u) {
+            for (int u = 0; u < BN_U; ++u) {
                 float b[8];
-                unpack8(v[u], IN, b);
-                const float *ar = la + (k + BN_KG * u) * MMAX;
+                unpack8<IN>(v[u], b);
 #pragma unroll
-                for (int m = 0; m < MMAX; ++m) {
-                    const float a = ar[m];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[m][c] = fmaf(a, b[c], acc[m][c]);
-                }
+                for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(a[u], b[j], acc[m][j]);
             }
         }
-        for (; k < klen; k += BN_KG) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(bcol + (int64_t)(kb + k) * p.b_rs);
-            float b[8];
-            unpack8(v, IN, b);
-            const float *ar = la + k * MMAX;
+    };
+
+    // Split and chunk boundaries are multiples of the sweep, so every sweep is
+    // whole except, possibly, the last one of K; only that one needs guards.
+    for (int c0 = kb; c0 < ke; c0 += p.kc) {
+        const int c1 = min(c0 + p.kc, ke);
+        const int clen = c1 - c0;
+        const int nfull = slab_full ? clen / BN_SWEEP : 0;   // whole sweeps of this chunk
+        // The first sweep's loads of B go out before A is staged.  They are
+        // issued unconditionally (from the 16-byte zero block when there is no
+        // whole sweep), so the wait for A below is exactly "all but these 8".
+        const bool first = nfull > 0;
+        const char *fb = first ? bcol + (int64_t)(c0 + lrow) * p.b_rs : reinterpret_cast<const char *>(&g_zero16);
+        const int64_t fs = first ? p.b_rs : 0;
+        u32x4 v[BN_U];
+
+        // Stage A[0..MMAX)[c0..c1) in LDS (rows >= M and k >= c1 as zeros).  With
+        // A rows K-contiguous, every thread first issues one 16-byte piece of A
+        // (threads past the end read the zero block and write a spare LDS slot),
+        // then the 8 loads of B, and only then stores A to LDS.
+        const int achunks = MMAX * (p.kc / 8);
+        auto a_chunk = [&](int idx, int &off) {
+            const int m = idx / (p.kc / 8), k = (idx - m * (p.kc / 8)) * 8;
+            off = m * p.kc + k;
+            const bool in = m < p.M && k < clen;
+            const char *q = in ? p.A + (int64_t)m * p.a_rs + (int64_t)(c0 + k) * 2
+                               : reinterpret_cast<const char *>(&g_zero16);
+            return *(const gu32x4 *)q;
+        };
+        auto a_fix = [&](u32x4 x, int off) {   // zero the values beyond the chunk end
+            const int k = off % p.kc;
+            if (k + 8 > clen) {
 #pragma unroll
-            for (int m = 0; m < MMAX; ++m)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[m][c] = fmaf(ar[m], b[c], acc[m][c]);
+                for (int q = 0; q < 4; ++q) {
+                    const int e = k + 2 * q;
+                    x[q] &= (e >= clen ? 0u : e + 1 >= clen ? 0xffffu : 0xffffffffu);
+                }
+            }
+            return x;
+        };
+        int a_off = 0;
+        u32x4 a_first = u32x4{0u, 0u, 0u, 0u};
+        if (p.a_vec) {
+            a_first = a_chunk(tid < achunks ? tid : 0, a_off);
+            if (tid >= achunks) a_off = MMAX * p.kc;   // the spare slot
         }
-    } else {
-        // ragged right edge: element loads, columns beyond N contribute nothing
-        for (int k = kg; k < klen; k += BN_KG) {
-            const float *ar = la + k * MMAX;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (n0 + c < p.N) {
-                    const float b = load_in(p.B + (int64_t)(kb + k) * p.b_rs + (int64_t)(n0 + c) * p.b_cs, IN);
+        for (int u = 0; u < BN_U; ++u)
+            v[u] = __builtin_nontemporal_load((const gu32x4 *)(fb + u * fs));
+        __builtin_amdgcn_sched_barrier(0);
+        if (c0 != kb) __syncthreads();   // the previous chunk's A is no longer read
+        if (p.a_vec) {
+            *reinterpret_cast<u32x4 *>(la + a_off) = a_fix(a_first, a_off);
+            for (int idx = tid + BN_NT; idx < achunks; idx += BN_NT) {
+                int off;
+                const u32x4 x = a_chunk(idx, off);
+                *reinterpret_cast<u32x4 *>(la + off) = a_fix(x, off);
+            }
+        } else {
+            for (int idx = tid; idx < MMAX * p.kc; idx += BN_NT) {
+                const int m = idx / p.kc, k = idx - m * p.kc;
+                uint16_t x = 0;
+                if (m < p.M && k < clen)
+                    x = *reinterpret_cast<const uint16_t *>(p.A + (int64_t)m * p.a_rs + (int64_t)(c0 + k) * p.a_cs);
+                la[idx] = x;
+            }
+        }
+        __syncthreads();
+
+        // whole sweeps: plain loads, then the multiply
+        for (int s = 0; s < nfull; ++s) {
+            const int k = s * BN_SWEEP + lrow;
+            if (s > 0) {
+                const char *q = bcol + (int64_t)(c0 + k) * p.b_rs;
 #pragma unroll
-                    for (int m = 0; m < MMAX; ++m) acc[m][c] = fmaf(ar[m], b, acc[m][c]);
+                for (int u = 0; u < BN_U; ++u)
+                    v[u] = __builtin_nontemporal_load((const gu32x4 *)(q + u * p.b_rs));
+            }
+            fma_sweep(v, k);
+        }
+        // the partial last sweep of K (full slab), with per-row guards
+        if (slab_full && nfull * BN_SWEEP < clen) {
+            const int k = nfull * BN_SWEEP + lrow;
+#pragma unroll
+            for (int u = 0; u < BN_U; ++u) {
+                v[u] = u32x4{0u, 0u, 0u, 0u};
+                if (k + u < clen) v[u] = *(const gu32x4 *)(bcol + (int64_t)(c0 + k + u) * p.b_rs);
+            }
+            fma_sweep(v, k);
+        }
+        if (!slab_full) {
+            // ragged right edge: element loads; columns beyond N contribute nothing
+            for (int k = lrow; k < clen; k += BN_SWEEP) {
+                for (int u = 0; u < BN_U && k + u < clen; ++u) {
+                    const char *q = p.B + (int64_t)(c0 + k + u) * p.b_rs;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (n0 + j < p.N) {
+                            const float b = to_f32<IN>(*reinterpret_cast<const uint16_t *>(q + (int64_t)(n0 + j) * p.b_cs));
+#pragma unroll
+                            for (int m = 0; m < MMAX; ++m)
+                                acc[m][j] = fmaf(to_f32<IN>(la[m * p.kc + k + u]), b, acc[m][j]);
+                        }
+                    }
                 }
             }
         }
     }
 
-    // Reduce the 8 K groups of a wave (lanes differing in bits 3..5), fixed order.
+    // Sum the two row groups of a wave (lanes c and c + 32), then the 8 waves
+    // through LDS: red[wave][m][BN_COLS], always in the same order.
 #pragma unroll
     for (int m = 0; m < MMAX; ++m)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float v = acc[m][c];
-            v += __shfl_xor(v, 8);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            acc[m][c] = v;
-        }
-    // Then the 4 waves through LDS: red[wave][m][64 columns].
-    __syncthreads();   // A slice no longer needed
-    float *red = la;
-    if (lane < 8) {
+        for (int j = 0; j < 8; ++j) acc[m][j] += __shfl_xor(acc[m][j], 32);
+    __syncthreads();   // the A chunk is no longer needed
+    if (lane < BN_W) {
 #pragma unroll
         for (int m = 0; m < MMAX; ++m)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) red[(wave * MMAX + m) * BN_COLS + lane * 8 + c] = acc[m][c];
+            for (int j = 0; j < 8; ++j) red[(wave * MMAX + m) * BN_COLS + lane * 8 + j] = acc[m][j];
     }
     __syncthreads();
-    for (int idx = tid; idx < MMAX * BN_COLS; idx += NT) {
-        const int m = idx / BN_COLS, col = idx - m * BN_COLS;
+    for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
+        const int m = t / BN_COLS, col = t - m * BN_COLS;
         const int n = blockIdx.x * BN_COLS + col;
-        if (m >= p.M || n >= p.N) continue;
-        float s = red[(0 * MMAX + m) * BN_COLS + col];
-        s += red[(1 * MMAX + m) * BN_COLS + col];
-        s += red[(2 * MMAX + m) * BN_COLS + col];
-        s += red[(3 * MMAX + m) * BN_COLS + col];
-        if (p.splits > 1) p.ws[((int64_t)z * p.M + m) * p.N + n] = s;
-        else epilogue_store(p.epi, m, n, s);
+        if (m < p.M && n < p.N) {
+            float s = red[m * BN_COLS + col];
+#pragma unroll
+            for (int w = 1; w < BN_WAVES; ++w) s += red[(w * MMAX + m) * BN_COLS + col];
+            if (p.splits > 1)   // agent-scope store: coherent across the XCDs' L2 caches
+                __hip_atomic_store(p.ws + ((int64_t)z * p.M + m) * p.N + n, s, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else epilogue_store(p.epi, m, n, s);
+        }
     }
+    if (p.splits == 1) return;
+
+    // K was split over grid.y: the last workgroup of this column slab to finish
+    // adds the S partials in the order s = 0..S-1 (so the bits do not depend on
+    // which workgroup finishes last), applies the epilogue, and re-arms the
+    // slab's counter for the next call on this stream.  The partials are
+    // written and read with agent-scope atomic accesses (coherent across the
+    // XCDs without writing back or invalidating whole L2 caches); each thread
+    // waits until its partial stores have completed before the workgroup takes
+    // its ticket, so the workgroup holding the last ticket sees every partial.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(p.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
+    __syncthreads();
+    if (!is_last) return;
+    for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
+        const int m = t / BN_COLS, col = t - m * BN_COLS;
+        const int n = blockIdx.x * BN_COLS + col;
+        if (m < p.M && n < p.N) {
+            float *w = p.ws + (int64_t)m * p.N + n;
+            float s = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q = 1; q < p.splits; ++q)
+                s += __hip_atomic_load(w + (int64_t)q * p.M * p.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            epilogue_store(p.epi, m, n, s);
+        }
+    }
+    if (tid == 0) __hip_atomic_store(p.counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ SK_BK
 
+// 512-wide K steps whose loads are in flight together (fewer for larger M, so
+// the A chunks still fit in registers)
+template <int MMAX> struct BkSteps { static constexpr int v = MMAX == 1 ? 8 : MMAX == 2 ? 4 : 2; };
+
 template <int MMAX, int IN>
-__global__ void __launch_bounds__(NT) skinny_bk(SkinnyArgs p) {
+__global__ void __launch_bounds__(256) skinny_bk(SkinnyArgs p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = blockIdx.x * (NT / 64) + wave;
+    const int n = blockIdx.x * (blockDim.x >> 6) + wave;
     const int z = blockIdx.y;
     const int kb = z * p.k_per_split;
     const int ke = min(kb + p.k_per_split, p.K);
@@ -178,27 +296,47 @@ __global__ void __launch_bounds__(NT) skinny_bk(SkinnyArgs p) {
     float acc[MMAX];
 #pragma unroll
     for (int m = 0; m < MMAX; ++m) acc[m] = 0.f;
-    // vector part: chunks of 8 K values, both A and B K-contiguous and aligned
+    // vector part: 16-byte chunks of 8 K values, A and B both K-contiguous and aligned
     const int kv_end = p.a_vec ? kb + ((ke - kb) / 8) * 8 : kb;
-    for (int k = kb + lane * 8; k < kv_end; k += 64 * 8) {
-        float b[8];
-        unpack8(*reinterpret_cast<const u32x4 *>(bcol + (int64_t)k * p.b_rs), IN, b);
+    constexpr int BK_STEPS = BkSteps<MMAX>::v;
+    for (int k0 = kb; k0 < kv_end; k0 += 512 * BK_STEPS) {
+        u32x4 bv[BK_STEPS], av[BK_STEPS][MMAX];
 #pragma unroll
-        for (int m = 0; m < MMAX; ++m) {
-            if (m < p.M) {
+        for (int t = 0; t < BK_STEPS; ++t) {
+            const int k = k0 + t * 512 + lane * 8;
+            if (k < kv_end) {
+                bv[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bcol + (int64_t)k * p.b_rs));
+#pragma unroll
+                for (int m = 0; m < MMAX; ++m)
+                    av[t][m] = (m < p.M) ? *reinterpret_cast<const u32x4 *>(p.A + (int64_t)m * p.a_rs + (int64_t)k * p.a_cs)
+                                         : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                bv[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int m = 0; m < MMAX; ++m) av[t][m] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < BK_STEPS; ++t) {
+            float b[8];
+            unpack8<IN>(bv[t], b);
+#pragma unroll
+            for (int m = 0; m < MMAX; ++m) {
                 float a[8];
-                unpack8(*reinterpret_cast<const u32x4 *>(p.A + (int64_t)m * p.a_rs + (int64_t)k * p.a_cs), IN, a);
+                unpack8<IN>(av[t][m], a);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[m] = fmaf(a[c], b[c], acc[m]);
+                for (int j = 0; j < 8; ++j) acc[m] = fmaf(a[j], b[j], acc[m]);
             }
         }
     }
     // scalar tail (or everything, if A is not K-contiguous)
     for (int k = kv_end + lane; k < ke; k += 64) {
-        const float b = load_in(bcol + (int64_t)k * p.b_rs, IN);
+        const float b = to_f32<IN>(*reinterpret_cast<const uint16_t *>(bcol + (int64_t)k * p.b_rs));
 #pragma unroll
         for (int m = 0; m < MMAX; ++m)
-            if (m < p.M) acc[m] = fmaf(load_in(p.A + (int64_t)m * p.a_rs + (int64_t)k * p.a_cs, IN), b, acc[m]);
+            if (m < p.M)
+                acc[m] = fmaf(to_f32<IN>(*reinterpret_cast<const uint16_t *>(p.A + (int64_t)m * p.a_rs + (int64_t)k * p.a_cs)),
+                              b, acc[m]);
     }
 #pragma unroll
     for (int m = 0; m < MMAX; ++m) {
@@ -219,42 +357,43 @@ __global__ void __launch_bounds__(NT) skinny_bk(SkinnyArgs p) {
 }
 
 template <int MMAX, int IN>
-hipError_t launch_k(int kind, const SkinnyArgs &a, int grid_x, hipStream_t s) {
+hipError_t launch_k(int kind, const SkinnyArgs &a, int grid_x, int waves, hipStream_t s) {
     dim3 grid(grid_x, a.splits);
     if (kind == SK_BN) {
-        const int kmax = a.k_per_split;
-        const int lds = max(kmax * MMAX * 4, 4 * MMAX * BN_COLS * 4);
-        auto k = skinny_bn<MMAX, IN>;
-        static int attr = 0;
-        if (lds > attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess) return e;
-            attr = lds;
+        const int lds = skinny_bn_lds(MMAX, a.kc);
+        if (lds > 48 * 1024) {
+            static int attr = 0;   // benign race: setting the attribute twice is harmless
+            if (lds > attr) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn<MMAX, IN>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                if (e != hipSuccess) return e;
+                attr = lds;
+            }
         }
-        hipLaunchKernelGGL(k, grid, dim3(NT), lds, s, a);
+        hipLaunchKernelGGL((skinny_bn<MMAX, IN>), grid, dim3(BN_NT), lds, s, a);
     } else {
-        hipLaunchKernelGGL((skinny_bk<MMAX, IN>), grid, dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((skinny_bk<MMAX, IN>), grid, dim3(64 * waves), 0, s, a);
     }
     return hipGetLastError();
 }
 
 template <int IN>
-hipError_t launch_m(int kind, int m_max, const SkinnyArgs &a, int grid_x, hipStream_t s) {
+hipError_t launch_m(int kind, int m_max, const SkinnyArgs &a, int grid_x, int waves, hipStream_t s) {
     switch (m_max) {
-    case 1: return launch_k<1, IN>(kind, a, grid_x, s);
-    case 2: return launch_k<2, IN>(kind, a, grid_x, s);
-    case 4: return launch_k<4, IN>(kind, a, grid_x, s);
-    case 8: return launch_k<8, IN>(kind, a, grid_x, s);
+    case 1: return launch_k<1, IN>(kind, a, grid_x, waves, s);
+    case 2: return launch_k<2, IN>(kind, a, grid_x, waves, s);
+    case 4: return launch_k<4, IN>(kind, a, grid_x, waves, s);
+    case 8: return launch_k<8, IN>(kind, a, grid_x, waves, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, hipStream_t stream) {
-    if (args.in_kind == IN_BF16) return launch_m<IN_BF16>(kind, m_max, args, grid_x, stream);
-    return launch_m<IN_F16>(kind, m_max, args, grid_x, stream);
+hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
+                         hipStream_t stream) {
+    if (args.in_kind == IN_BF16) return launch_m<IN_BF16>(kind, m_max, args, grid_x, waves, stream);
+    return launch_m<IN_F16>(kind, m_max, args, grid_x, waves, stream);
 }
 
 }  // namespace dg

@@ -37,8 +37,10 @@
  *    during execution surface at the caller's next synchronization.
  *  - On any error return, C has not been touched and nothing was enqueued.
  *  - Thread safety: every entry point may be called concurrently from several
- *    host threads and on several streams.  Split-K scratch memory is taken
- *    stream-ordered (hipMallocAsync/hipFreeAsync on `stream`).
+ *    host threads and on several streams.  Split-K scratch memory is a
+ *    library-owned device buffer per (device, stream), allocated with hipMalloc
+ *    on first need, grown on demand (after waiting for that stream) and kept
+ *    until the process ends; calls on different streams never share one.
  */
 #ifndef DG_H
 #define DG_H

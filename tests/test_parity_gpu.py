@@ -186,3 +186,40 @@ def test_workload_fp32_c_literal_bound(dg, name):
     c = synth.Case(name + "_f32", case.A, case.B, torch.full((M, N), float("nan")), case.alpha,
                    case.beta, case.A_scale, case.B_scale, case.rtol)
     check(dg, c, rows=None if M <= 64 else _sample_rows(M, seed=3), literal=True)
+
+
+# ---------------------------------------------------------------- the streaming (skinny) kernels
+
+def _plan_field(dg, case, name):
+    import re
+    d = case.to(DEV)
+    text = dg.plan(d.A, d.B, d.C, case.alpha, case.beta, d.A_scale, d.B_scale)
+    m = re.search(r"\b" + name + r"=(\S+)", text)
+    return m.group(1) if m else None, text
+
+
+@pytest.mark.parametrize("nk", [(64, 8), (1000, 777), (4104, 4096), (200, 17000), (14336, 520), (96, 4096)],
+                         ids=lambda t: f"N{t[0]}K{t[1]}")
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_skinny_bn(dg, M, nk):
+    # B row-major (N-contiguous): ragged slabs, K tails, several LDS chunks of A,
+    # and the split-K fallback when there are few column slabs.
+    N, K = nk
+    dtype = BF16 if (M + N) % 2 else F16
+    c = synth.gemm_case(M, N, K, dtype, BF16 if M % 2 else torch.float32, seed=M * 31 + N + K,
+                        alpha=1.0 if M != 3 else -0.5, beta=0.0 if M != 5 else 1.0)
+    kind, text = _plan_field(dg, c, "kind")
+    assert "path=skinny" in text and kind == "BN", text
+    check(dg, c)
+
+
+@pytest.mark.parametrize("nk", [(1, 8), (128, 4096), (129, 1000), (1500, 4104), (7, 9000)],
+                         ids=lambda t: f"N{t[0]}K{t[1]}")
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_skinny_bk(dg, M, nk):
+    # B = K_cache^T (K-contiguous columns), as in the query x key-cache product.
+    N, K = nk
+    c = synth.gemm_case(M, N, K, BF16, BF16, seed=M * 7 + N + K, b_layout="col")
+    kind, text = _plan_field(dg, c, "kind")
+    assert "path=skinny" in text and kind == "BK", text
+    check(dg, c)
