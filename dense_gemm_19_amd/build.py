@@ -22,10 +22,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+# Per-source extra flags.  The FP8 kernels promote each matrix-core block sum on
+# the vector ALUs; the VGPR form of the MFMA instructions lets those sums land
+# where the ALUs can use them (no copies out of accumulation registers).
+EXTRA_FLAGS = {"gemm_dtl_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
-HIP_SOURCES = ["gemm_mfma.hip", "skinny.hip", "epilogue.hip"]
-HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp"]
+HIP_SOURCES = ["gemm_mfma.hip", "gemm_dtl_f16.hip", "gemm_dtl_bf16.hip", "gemm_dtl_f8.hip", "skinny.hip",
+               "epilogue.hip"]
+HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp", "gemm_dtl.cpp"]
 
 
 def _newest_header() -> float:
@@ -41,7 +46,7 @@ def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
         if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
             return obj
     flags = HIP_FLAGS if src.endswith(".hip") else HOST_FLAGS
-    cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + flags + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

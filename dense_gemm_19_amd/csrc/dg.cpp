@@ -251,7 +251,8 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         a.kt_per_split = pl.kt_per_split;
         a.splits = pl.splits;
         a.group_m = pl.group_m;
-        e = launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
+        e = pl.dtl ? launch_mfma_dtl(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, a, stream)
+                   : launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
     }
     // split-K partials are summed by a second kernel, except where the streaming
     // kernel sums them itself (its last workgroup per column slab)

@@ -1,0 +1,22 @@
+// gemm_dtl.cpp -- dispatch of the direct-to-LDS matrix-core kernels by input type.
+#include "kernels.hpp"
+
+namespace dg {
+
+hipError_t launch_mfma_dtl_f16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
+hipError_t launch_mfma_dtl_bf16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
+hipError_t launch_mfma_dtl_f8(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
+
+bool mfma_dtl_tile(int tile) { return tile == T256x256 || tile == T128x128; }
+
+hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const MfmaArgs &args,
+                           hipStream_t stream) {
+    switch (in_kind) {
+    case IN_F16: return launch_mfma_dtl_f16(tile, a_mode, b_mode, args, stream);
+    case IN_BF16: return launch_mfma_dtl_bf16(tile, a_mode, b_mode, args, stream);
+    case IN_F8: return launch_mfma_dtl_f8(tile, a_mode, b_mode, args, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg

@@ -1,0 +1,11 @@
+// gemm_dtl_f16.hip -- the direct-to-LDS matrix-core kernels for f16 inputs
+// (see gemm_dtl.hpp).
+#include "gemm_dtl.hpp"
+
+namespace dg {
+
+hipError_t launch_mfma_dtl_f16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream) {
+    return dtl::launch_tiles<IN_F16>(tile, a_mode, b_mode, args, stream);
+}
+
+}  // namespace dg

@@ -104,6 +104,11 @@ enum SkinnyKind : int { SK_BN = 0 /* B N-contiguous */, SK_BK = 1 /* B K-contigu
 hipError_t launch_mfma(int in_kind, int tile, int a_mode, int b_mode, int slow,
                        const MfmaArgs &args, hipStream_t stream);
 // waves: SK_BK waves (columns) per workgroup; ignored by SK_BN.
+// Matrix-core kernel with direct HBM -> LDS tile loads (gemm_dtl.hip): needs
+// 16-byte chunks (vec) on both operands and K a multiple of the K tile.
+bool mfma_dtl_tile(int tile);
+hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const MfmaArgs &args,
+                           hipStream_t stream);
 hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);

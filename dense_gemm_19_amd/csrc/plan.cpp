@@ -15,6 +15,7 @@ struct Overrides {
     int force_splitk = 0;
     int force_tile = -1;
     bool no_vec = false;
+    bool no_dtl = false;
     bool log = false;
 };
 
@@ -34,6 +35,7 @@ const Overrides &overrides() {
             }
         }
         if (const char *s = std::getenv("DG_NO_VEC")) r.no_vec = s[0] == '1';
+        if (const char *s = std::getenv("DG_NO_DTL")) r.no_dtl = s[0] == '1';
         if (const char *s = std::getenv("DG_LOG")) r.log = s[0] == '1';
         return r;
     }();
@@ -135,6 +137,9 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
         int64_t best_tiles = -1;
         bool found = false;
         for (int t : order) {
+            // FP8 256x256: the per-K-block promotion of a 128x64 wave tile does not
+            // fit the registers of two waves per SIMD (it spills), so stop at 128
+            if (p.fp8 && t == T256x256) continue;
             const int64_t tm = cdiv(p.M, mfma_tile_bm(t)), tn = cdiv(p.N, mfma_tile_bn(t));
             const int64_t nt = tm * tn;
             // skip macro tiles that would be more than a quarter padding
@@ -160,6 +165,7 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     pl.splits = (int)cdiv(std::max(pl.ktiles, 1), pl.kt_per_split);
     pl.group_m = std::min(pl.tiles_m, 4);
     pl.lds_bytes = mfma_tile_lds(pl.slow ? T64x64 : tile, p.fp8);
+    pl.dtl = !pl.slow && mfma_dtl_tile(tile) && p.K % kel == 0 && !overrides().no_dtl;
 }
 
 }  // namespace
@@ -245,10 +251,10 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
             pl.splits, pl.sk_kc, pl.sk_kind == SK_BN ? SKINNY_BN_THREADS / 64 : pl.sk_waves, pl.sk_a_vec, pl.lds_bytes);
         break;
     case Path::Mfma:
-        add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d tiles=%dx%d ktiles=%d splits=%d "
+        add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d dtl=%d tiles=%dx%d ktiles=%d splits=%d "
             "kt_per_split=%d group_m=%d grid=%dx1x%d lds=%d",
             mfma_tile_bm(pl.slow ? T64x64 : pl.tile), mfma_tile_bn(pl.slow ? T64x64 : pl.tile),
-            modes[pl.a.mode], modes[pl.b.mode], (int)pl.a.vec, (int)pl.b.vec, pl.slow, pl.tiles_m,
+            modes[pl.a.mode], modes[pl.b.mode], (int)pl.a.vec, (int)pl.b.vec, pl.slow, pl.dtl, pl.tiles_m,
             pl.tiles_n, pl.ktiles, pl.splits, pl.kt_per_split, pl.group_m, pl.tiles_m * pl.tiles_n,
             pl.splits, pl.lds_bytes);
         break;

@@ -161,7 +161,7 @@ def gemm_case(M, N, K, in_dtype=torch.bfloat16, out_dtype=torch.float32, seed=0,
 
 
 def fp8_case(M, N, K, seed=0, out_dtype=torch.bfloat16, alpha=1.0, beta=0.0, dist="normal",
-             scale=1.0, b_layout="row", name=None) -> Case:
+             scale=1.0, b_layout="row", a_layout="row", name=None) -> Case:
     """An FP8 E4M3 case: sources drawn, then quantized per token and per block."""
     g = rng(seed)
     a_src = torch.from_numpy(draw(g, (M, K), dist, scale))
@@ -173,6 +173,8 @@ def fp8_case(M, N, K, seed=0, out_dtype=torch.bfloat16, alpha=1.0, beta=0.0, dis
     qb, sb = quantize_blocks_128(b_src.contiguous())
     if b_layout == "col":
         qb = qb.t().contiguous().t()
+    if a_layout == "col":   # same values, stored column-major
+        qa = qa.t().contiguous().t()
     if beta != 0.0:
         c = to_dtype(draw(g, (M, N), "normal", 1.0), out_dtype)
     else:

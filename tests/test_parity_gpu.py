@@ -223,3 +223,27 @@ def test_skinny_bk(dg, M, nk):
     kind, text = _plan_field(dg, c, "kind")
     assert "path=skinny" in text and kind == "BK", text
     check(dg, c)
+
+
+# ---------------------------------------------------------------- the direct-to-LDS matrix-core kernels
+
+@pytest.mark.parametrize("shape", [(1000, 4104, 512), (4000, 4096, 256)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("layouts", [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")],
+                         ids=lambda l: "A" + l[0] + "-B" + l[1])
+@pytest.mark.parametrize("kind", ["f16", "bf16", "fp8"])
+def test_dtl_tiles(dg, kind, layouts, shape):
+    # 128x128 and 256x256 macro tiles with M and N edges that cut through a tile,
+    # every operand storage order, every input type; K a whole number of tiles.
+    M, N, K = shape
+    if kind == "fp8" and M == 1000:   # 1-byte elements: 16-element chunks need M, N multiples of 16
+        M, N = 1008, 4112
+    seed = M + N + K + len(kind) + 3 * len(layouts[0]) + len(layouts[1])
+    if kind == "fp8":
+        c = synth.fp8_case(M, N, K, seed=seed, a_layout=layouts[0], b_layout=layouts[1],
+                           out_dtype=torch.float32, beta=0.5)
+    else:
+        c = synth.gemm_case(M, N, K, F16 if kind == "f16" else BF16, BF16, seed=seed,
+                            a_layout=layouts[0], b_layout=layouts[1], alpha=1.5)
+    dtl, text = _plan_field(dg, c, "dtl")
+    assert dtl == "1", text
+    check(dg, c, rows=_sample_rows(M, seed=seed))
