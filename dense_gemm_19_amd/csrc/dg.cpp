@@ -245,6 +245,7 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         a.sb_rs = p.SB.rs; a.sb_cs = p.SB.cs;
         a.epi = epi;
         a.ws = ws;
+        a.counters = counters;
         a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
         a.tiles_m = pl.tiles_m; a.tiles_n = pl.tiles_n;
         a.ktiles = pl.ktiles;
@@ -256,7 +257,7 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
     }
     // split-K partials are summed by a second kernel, except where the streaming
     // kernel sums them itself (its last workgroup per column slab)
-    const bool fused = pl.path == Path::Skinny && pl.sk_kind == SK_BN;
+    const bool fused = (pl.path == Path::Skinny && pl.sk_kind == SK_BN) || (pl.path == Path::Mfma && pl.dtl);
     if (e == hipSuccess && pl.splits > 1 && !fused) {
         ReduceArgs r{ws, epi, (int)p.M, (int)p.N, pl.splits};
         e = launch_reduce(r, stream);

@@ -7,7 +7,7 @@ hipError_t launch_mfma_dtl_f16(int tile, int a_mode, int b_mode, const MfmaArgs 
 hipError_t launch_mfma_dtl_bf16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
 hipError_t launch_mfma_dtl_f8(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
 
-bool mfma_dtl_tile(int tile) { return tile == T256x256 || tile == T128x128; }
+bool mfma_dtl_tile(int tile) { return tile >= 0 && tile < NUM_MFMA_TILES; }
 
 hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const MfmaArgs &args,
                            hipStream_t stream) {

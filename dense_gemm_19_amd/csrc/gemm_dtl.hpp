@@ -24,6 +24,8 @@
 // gfx950 LDS transpose reads for M/N-contiguous ones), the XCD-aware tile
 // raster and the epilogue are those of gemm_mfma.hip.
 #pragma once
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace dg {
@@ -42,11 +44,16 @@ template <> struct InT<IN_F8>   { static constexpr int EB = 1; static constexpr 
 
 __device__ __forceinline__ int kmaj_off(int r, int c) { return r * KBYTES + ((c ^ (r & 7)) << 4); }
 
+// XOR swizzle of the 16-byte chunks of K row k (M/N-contiguous operands).  The
+// transpose reads of one 16-lane group touch 4 (16-bit) or 8 (8-bit) consecutive
+// K rows; the swizzle spreads those rows, and the K rows of the wave's other
+// lane groups (K bits 3-4 for 16-bit, 5-6 for 8-bit), over distinct banks.
 template <int EB, int CPR>
 __device__ __forceinline__ int mn_swz(int k) {
     int s;
     if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
-    else s = (k & 7) | (((k >> 5) & 3) << 3);
+    else if (CPR >= 32) s = (k & 7) | (((k >> 5) & 3) << 3);
+    else s = (k & 7) ^ ((k >> 5) & 3) ^ (CPR >= 16 ? ((k >> 5) & 1) << 3 : 0);
     return s & (CPR - 1);
 }
 template <int EB, int R>
@@ -56,6 +63,28 @@ __device__ __forceinline__ int mnmaj_off(int k, int c) {
 }
 
 // ------------------------------------------------------------------ HBM -> LDS
+
+// One load-to-LDS instruction: lane i's `size` bytes from g land at LDS address
+// lds + size*i (lds must be wave-uniform).  Written as inline assembly so that
+// the compiler's own wait insertion does not treat it as an LDS store that every
+// later LDS read must wait for (it cannot tell the ring's stages apart across
+// the loop back-edge); the kernel waits for these loads itself, with exact
+// counts.  The memory clobber keeps other memory accesses in program order
+// around it.  Every vector-memory instruction of the main loop is one of these,
+// so the kernel's counts are exact; any wait the compiler adds for its own
+// loads can only be stricter, since these are in-order counters.
+__device__ __forceinline__ void lds_load16(const void *g, const char *lds) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void *g, const char *lds) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(a), "v"(g)
+                 : "memory", "m0");
+}
 
 // One operand's K tile: R rows (M for A, N for B) x 128 bytes of K, 8*R chunks
 // of 16 bytes, i.e. R/8 load instructions of a wave (64 chunks each), shared
@@ -87,7 +116,7 @@ struct DtlIO {
             // MNMAJ, where a chunk spans EPC rows); their results are not stored
             const int gr = min(r0 + r, MODE == KMAJ ? Rlim - 1 : Rlim - EPC);
             const char *src = op.ptr + (int64_t)gr * op.r_stride + (int64_t)(k0 + k) * op.k_stride;
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(lds + blk * 1024), 16, 0, 0);
+            lds_load16(src, lds + blk * 1024);
         }
     }
 };
@@ -166,55 +195,44 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
     tn = in / gsz;
 }
 
-// ------------------------------------------------------------------ epilogue (as gemm_mfma.hip)
-
-template <int TM, int TN, int OUTK>
-__device__ __forceinline__ void write_tile(const f32x4 (&acc)[TM][TN], const MfmaArgs &p, int mb, int nb,
-                                           int z) {
-    const Epilogue &ep = p.epi;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = nb + 16 * j;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = mb + 16 * i + e;
-                if (m < p.M && n < p.N) {
-                    const float a = acc[i][j][e];
-                    if (OUTK < 0) {
-                        p.ws[((int64_t)z * p.M + m) * p.N + n] = a;
-                    } else {
-                        char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
-                        float v = ep.alpha * a;
-                        if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, OUTK), v);
-                        store_out(q, OUTK, v);
-                    }
-                }
-            }
-        }
-}
-
 // ------------------------------------------------------------------ the kernel
 
-// The two LDS stages are separate __shared__ arrays and the K loop is unrolled
-// by two, so the compiler can see that the loads filling one stage never alias
-// the fragment reads of the other, and need not wait for them before reading.
-template <int IN, int BM, int BN, int WGM, int WGN, int AMODE, int BMODE>
+// An NS-stage LDS ring.  The loads filling a stage are load-to-LDS
+// instructions the compiler does not track (see lds_load16), so nothing makes
+// a fragment read wait for loads into other stages; before the barrier that
+// opens tile kt, each wave waits (explicit vmcnt) for its own loads into that
+// tile's stage: exactly the loads of the later tiles may still be in flight.
+//
+// FP8 scales ride along in every stage: BM row scales sA[m][kt] and up to 64
+// column-block scales sB[kt][nb], each staged with 4-byte load-to-LDS
+// instructions (every wave issues the same two, so all waves count the same
+// number of loads per tile).
+//
+// Split-K (grid.z = S > 1): each workgroup writes its FP32 partial tile with
+// agent-scope stores; the last of the S workgroups of a tile (arrival counter)
+// sums the partials in the order s = 0..S-1, applies the epilogue, and re-arms
+// the counter (sheratonhq.com deep dive, section 5.2, with a fixed summation
+// order so that the bits do not depend on which workgroup finishes last).
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
-    constexpr int NW = WGM * WGN, NT = 64 * NW;
+    constexpr int NW = WGM * WGN;
     constexpr int EB = InT<IN>::EB;
     constexpr bool F8 = (IN == IN_F8);
     constexpr int A_BYTES = BM * KBYTES, B_BYTES = BN * KBYTES;
-    constexpr int STAGE = A_BYTES + B_BYTES + (F8 ? BM * 4 : 0);
+    constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + (F8 ? BM * 4 : 0);
+    constexpr int STAGE = SB_OFF + (F8 ? 256 : 0);
     constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 16, TN = WTN / 16;
     constexpr int KEL = KBYTES / EB;
-    static_assert(BM <= NT || !F8, "one thread per row scale");
-    static_assert(WTN <= 128, "a wave's columns lie in one 128-column scale block");
     using AIO = DtlIO<AMODE, BM, EB, NW>;
     using BIO = DtlIO<BMODE, BN, EB, NW>;
-    __shared__ __attribute__((aligned(16))) char stage0[STAGE];
-    __shared__ __attribute__((aligned(16))) char stage1[STAGE];
+    constexpr int PER_FILL = AIO::INSTS + BIO::INSTS + (F8 ? 2 : 0);   // loads per wave per tile
+    static_assert(NS >= 2 && NS <= 8, "2..8 stages");
+    static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns lie in one 128-column scale block");
+    static_assert(BM % 64 == 0 || !F8, "row scales are staged 64 per wave");
+    static_assert((NS - 2) * PER_FILL <= 63, "vmcnt range");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
+    __shared__ int is_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
@@ -231,30 +249,27 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // FP8 scales: one row scale per thread (threads < BM) per K block, staged in
-    // LDS beside the tile, and the wave's column-block scale.
-    float sa_reg = 0.f, sb_reg = 0.f;
-    const int sa_row = m0 + tid;
-    const int wave_n0 = n0 + wn * WTN;
-    auto load_scales = [&](int kt) {
-        if (F8) {
-            if (tid < BM && sa_row < p.M)
-                sa_reg = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.sa) +
-                                                          (int64_t)sa_row * p.sa_rs + (int64_t)kt * p.sa_cs);
-            if (wave_n0 < p.N)
-                sb_reg = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.sb) +
-                                                          (int64_t)kt * p.sb_rs + (int64_t)(wave_n0 >> 7) * p.sb_cs);
-        }
-    };
-    auto fill = [&](char *st, int kt) {   // issue the loads of K tile kt into stage st
+    // FP8 scale sources of this thread's lane for the staging loads
+    const int NBLK = (p.N + 127) >> 7;
+    const int sa_row = min(m0 + 64 * (wave % (F8 ? BM / 64 : 1)) + lane, p.M - 1);
+    const int sb_blk = min((n0 >> 7) + lane, NBLK - 1);
+
+    auto fill = [&](char *st, int kt) __attribute__((always_inline)) {   // issue the loads of K tile kt into stage st
         AIO::issue(st, p.a, m0, kt * KEL, p.M, wave, lane);
         BIO::issue(st + A_BYTES, p.b, n0, kt * KEL, p.N, wave, lane);
-        load_scales(kt);
+        if constexpr (F8) {
+            const char *sa = reinterpret_cast<const char *>(p.sa) + (int64_t)sa_row * p.sa_rs + (int64_t)kt * p.sa_cs;
+            const char *sb = reinterpret_cast<const char *>(p.sb) + (int64_t)kt * p.sb_rs + (int64_t)sb_blk * p.sb_cs;
+            lds_load4(sa, st + SA_OFF + 256 * (wave % (BM / 64)));
+            lds_load4(sb, st + SB_OFF);
+        }
     };
-    auto compute = [&](const char *la, float sb_cur) {
+
+    auto compute = [&](const char *la) __attribute__((always_inline)) {
         const char *lb = la + A_BYTES;
         if constexpr (F8) {
-            const float *lsa = reinterpret_cast<const float *>(la + A_BYTES + B_BYTES);
+            const float *lsa = reinterpret_cast<const float *>(la + SA_OFF);
+            const float sb = reinterpret_cast<const float *>(la + SB_OFF)[(wn * WTN) >> 7];
             i32x8 fb[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j) fb[j] = frag8<BMODE, BN>(lb, wn * WTN + 16 * j, lane);
@@ -262,7 +277,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             for (int i = 0; i < TM; ++i) {
                 const i32x8 fa = frag8<AMODE, BM>(la, wm * WTM + 16 * i, lane);
                 const f32x4 sa4 = *reinterpret_cast<const f32x4 *>(lsa + wm * WTM + 16 * i + 4 * (lane >> 4));
-                const f32x4 s4 = sa4 * sb_cur;
+                const f32x4 s4 = sa4 * sb;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     // block sum over this 128-wide K block on the matrix cores, then
@@ -273,17 +288,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
                     for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(s4[e], blk[e], acc[i][j][e]);
                 }
             }
-            // Interleave each matrix-core block sum with the four promotions of an
-            // earlier one, so only a few block results are live at a time (left
-            // alone, the scheduler issues every block sum first and runs out of
-            // registers).
-#pragma unroll
-            for (int t = 0; t < TM * TN; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-            }
         } else {
-            (void)sb_cur;
 #pragma unroll
             for (int ks = 0; ks < InT<IN>::KSTEPS; ++ks) {
                 // the wave's B fragments of this K step stay in registers; A
@@ -300,62 +305,173 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             }
         }
     };
-    // one K tile: start filling `nxt` with tile kt+1 (if any), multiply `cur`,
-    // stage the next row scales, wait for this thread's loads, then sync
-    auto step = [&](const char *cur, char *nxt, int kt) {
-        const bool more = kt + 1 < kt1;
-        const float sb_cur = sb_reg;
-        if (more) fill(nxt, kt + 1);
-        compute(cur, sb_cur);
-        if (F8 && more && tid < BM) *reinterpret_cast<float *>(nxt + A_BYTES + B_BYTES + 4 * tid) = sa_reg;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+
+    // wait until at most `later` tiles' loads of this wave are still in flight
+    auto wait_tiles = [&](int later) __attribute__((always_inline)) {
+        constexpr int enc0 = (0x7 << 4) | (0xF << 8);   // expcnt, lgkmcnt: no wait
+#define DG_VMCNT(n) (((n) & 0xF) | (((n) >> 4) << 14) | enc0)
+        switch (later) {
+        case 0: __builtin_amdgcn_s_waitcnt(DG_VMCNT(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 2 ? 1 * PER_FILL : 0)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 3 ? 2 * PER_FILL : 0)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 4 ? 3 * PER_FILL : 0)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 5 ? 4 * PER_FILL : 0)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 6 ? 5 * PER_FILL : 0)); break;
+        default: __builtin_amdgcn_s_waitcnt(DG_VMCNT(NS > 7 ? 6 * PER_FILL : 0)); break;
+        }
+#undef DG_VMCNT
     };
 
-    if (kt0 < kt1) {
-        fill(stage0, kt0);
-        if (F8 && tid < BM) *reinterpret_cast<float *>(stage0 + A_BYTES + B_BYTES + 4 * tid) = sa_reg;
+    // prologue: the first NS - 1 tiles go out
+#pragma unroll
+    for (int q = 0; q + 1 < NS; ++q)
+        if (kt0 + q < kt1) fill(ring + q * STAGE, kt0 + q);
+    // tile kt sits in stage `cur`; the stage freed by tile kt - 1 takes tile kt + NS - 1
+    auto body = [&](int cur, int kt) __attribute__((always_inline)) {
+        wait_tiles(min(NS - 2, kt1 - 1 - kt));
+        // A plain barrier: __syncthreads() would add a wait for every outstanding
+        // load-to-LDS (they count as LDS writes), draining the ring.  This wave's
+        // loads into tile kt are complete (wait above); the memory clobber keeps
+        // the compiler from moving LDS accesses or the refill across it; the
+        // previous stage's reads have all been consumed by matrix instructions.
+        asm volatile("s_barrier" ::: "memory");
+        const int nxt = cur == 0 ? NS - 1 : cur - 1;
+        if (kt + NS - 1 < kt1) fill(ring + nxt * STAGE, kt + NS - 1);
+        compute(ring + cur * STAGE);
+    };
+    // (a rolled loop: unrolling it, even by two for NS = 2, pushes the 256x256
+    // tile's 8-wave kernel past its 256 registers and it spills)
+    int cur = 0;
+    for (int kt = kt0; kt < kt1; ++kt) {
+        body(cur, kt);
+        cur = cur + 1 == NS ? 0 : cur + 1;
     }
+
+    // ---- epilogue: element (i, j, e) of a wave is C[mb + 16i + e][nb + 16j]
+    const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
+    const Epilogue &ep = p.epi;
+    auto store = [&](auto OUTK, int m, int n, float a) __attribute__((always_inline)) {
+        constexpr int ok = decltype(OUTK)::value;
+        char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
+        float v = ep.alpha * a;
+        if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, ok), v);
+        store_out(q, ok, v);
+    };
+    auto finish = [&](auto OUTK) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = nb + 16 * j;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = mb + 16 * i + e;
+                    if (m < p.M && n < p.N) store(OUTK, m, n, acc[i][j][e]);
+                }
+            }
+    };
+    auto finish_any = [&]() __attribute__((always_inline)) {
+        if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{});
+        else if (ep.out_kind == OUT_BF16) finish(std::integral_constant<int, OUT_BF16>{});
+        else finish(std::integral_constant<int, OUT_F16>{});
+    };
+    // Split K is a separate instantiation (SPLIT), so that the kernels without
+    // it keep their registers; it exists for tiles of at most 64 accumulator
+    // registers per lane (the reduction stages partials beside them).
+    static_assert(!SPLIT || TM * TN <= 16, "split K only for small tiles");
+    if (!SPLIT) {
+        finish_any();
+        return;
+    }
+    // split K: publish this workgroup's partial tile (agent-scope stores are
+    // coherent across the XCDs' L2 caches), wait for the stores, take a ticket
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = nb + 16 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = mb + 16 * i + e;
+                if (m < p.M && n < p.N)
+                    __hip_atomic_store(p.ws + ((int64_t)z * p.M + m) * p.N + n, acc[i][j][e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int kt = kt0;
-    for (; kt + 1 < kt1; kt += 2) {
-        step(stage0, stage1, kt);
-        step(stage1, stage0, kt + 1);
+    const int tile = tm * p.tiles_n + tn;
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  p.splits - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // The sum runs over s = 0..S-1 in order, this workgroup's own partial
+    // included; for each s all of the thread's elements are loaded together
+    // (one round trip per split, not one per split and element).
+    auto part = [&](int q, int m, int n) __attribute__((always_inline)) {
+        return __hip_atomic_load(p.ws + ((int64_t)q * p.M + min(m, p.M - 1)) * p.N + min(n, p.N - 1),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, mb + 16 * i + e, nb + 16 * j);
+    for (int q = 1; q < p.splits; ++q) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {   // a 16-row block of partials at a time
+            f32x4 v[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[j][e] = part(q, mb + 16 * i + e, nb + 16 * j);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] += v[j];
+        }
     }
-    if (kt < kt1) step(stage0, stage1, kt);
-
-    const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
-    if (p.splits > 1) write_tile<TM, TN, -1>(acc, p, mb, nb, z);
-    else if (p.epi.out_kind == OUT_F32) write_tile<TM, TN, OUT_F32>(acc, p, mb, nb, z);
-    else if (p.epi.out_kind == OUT_BF16) write_tile<TM, TN, OUT_BF16>(acc, p, mb, nb, z);
-    else write_tile<TM, TN, OUT_F16>(acc, p, mb, nb, z);
+    finish_any();
+    if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int AM, int BMd>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd>
 hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
-    auto k = mfma_dtl<IN, BM, BN, WGM, WGN, AM, BMd>;
+    constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
     dim3 grid(a.tiles_m * a.tiles_n, 1, a.splits);
-    hipLaunchKernelGGL(k, grid, dim3(64 * WGM * WGN), 0, s, a);
+    if (a.splits > 1) {
+        if constexpr (TM * TN <= 16) {
+            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true>), grid, dim3(64 * WGM * WGN), 0, s, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;   // no split K for this tile (the planner never asks)
+        }
+    }
+    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false>), grid, dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS>
 hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
-    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, KMAJ, KMAJ>(a, s);
-    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, KMAJ, MNMAJ>(a, s);
-    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, MNMAJ, KMAJ>(a, s);
-    return launch_t<IN, BM, BN, WGM, WGN, MNMAJ, MNMAJ>(a, s);
+    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ>(a, s);
+    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ>(a, s);
+    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ>(a, s);
+    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ>(a, s);
 }
 
+// Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64 with 2
+// stages; 128x128 4 waves of 64x64 with 2 stages; the small tiles, used for
+// HBM-bound shapes with few rows, 4 waves with deep rings (6 or 8 stages), so
+// that enough bytes stream per CU to cover the memory latency (64x128 runs as
+// 1 x 4 waves of 64x32, so each stage carries twice as much of B as of A).
 template <int IN>
 hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
     switch (tile) {
-    // 8 waves (2 per SIMD) of 128x64: the FP8 promotion runs on the vector ALUs,
-    // which cannot address accumulation registers, so a wave's accumulators must
-    // fit in its share of the vector registers alongside everything else
-    case T256x256: return launch_modes<IN, 256, 256, 2, 4>(am, bm, a, s);
-    case T128x128: return launch_modes<IN, 128, 128, 2, 2>(am, bm, a, s);
+    case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
+    case T128x128: return launch_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, s);
+    case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
+    case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);
+    case T64x128: return launch_modes<IN, 64, 128, 1, 4, 6>(am, bm, a, s);
     }
     return hipErrorInvalidValue;
 }

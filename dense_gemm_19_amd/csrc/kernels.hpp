@@ -42,6 +42,7 @@ struct MfmaArgs {
     const float *sb; int64_t sb_rs, sb_cs;   // FP8 only: [KB][NB] scales (bytes)
     Epilogue epi;
     float *ws;                  // split-K partials [S][M][N] FP32, or null when S == 1
+    int *counters;              // direct-to-LDS kernel, S > 1: one per tile, 0 on entry and exit
     int M, N, K;
     int tiles_m, tiles_n;
     int ktiles;                 // ceil(K / BK)
@@ -89,9 +90,10 @@ struct ScaleArgs {      // C <- beta * C (beta == 0: C <- 0), for alpha == 0 or 
 };
 
 // Tile configurations of the matrix-core kernel (index = MfmaTile).
-enum MfmaTile : int { T256x256 = 0, T128x128 = 1, T64x64 = 2, T128x64 = 3, NUM_MFMA_TILES = 4 };
-inline int mfma_tile_bm(int t) { const int v[] = {256, 128, 64, 128}; return v[t]; }
-inline int mfma_tile_bn(int t) { const int v[] = {256, 128, 64, 64}; return v[t]; }
+// T64x128 exists only in the direct-to-LDS kernel (gemm_dtl.hpp).
+enum MfmaTile : int { T256x256 = 0, T128x128 = 1, T64x64 = 2, T128x64 = 3, T64x128 = 4, NUM_MFMA_TILES = 5 };
+inline int mfma_tile_bm(int t) { const int v[] = {256, 128, 64, 128, 64}; return v[t]; }
+inline int mfma_tile_bn(int t) { const int v[] = {256, 128, 64, 64, 128}; return v[t]; }
 // LDS bytes: two stages of (BM + BN) rows x 128 bytes of K (+ BM FP32 row scales for FP8).
 inline int mfma_tile_lds(int t, bool fp8) {
     return 2 * ((mfma_tile_bm(t) + mfma_tile_bn(t)) * 128 + (fp8 ? mfma_tile_bm(t) * 4 : 0));

@@ -121,6 +121,16 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
     return false;
 }
 
+// Fraction of a tile grid's area that is real (not padding past M or N).
+double tile_eff(int64_t M, int64_t N, int t) {
+    const int64_t tm = cdiv(M, mfma_tile_bm(t)), tn = cdiv(N, mfma_tile_bn(t));
+    return (double)M * (double)N / ((double)tm * mfma_tile_bm(t) * (double)tn * mfma_tile_bn(t));
+}
+
+int64_t tile_count(int64_t M, int64_t N, int t) {
+    return cdiv(M, mfma_tile_bm(t)) * cdiv(N, mfma_tile_bn(t));
+}
+
 void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     const int epc = p.fp8 ? 16 : 8;              // elements per 16-byte chunk
     const int kel = p.fp8 ? 128 : 64;            // K elements per tile
@@ -130,42 +140,74 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     if (overrides().no_vec) pl.a.vec = pl.b.vec = false;
     pl.slow = !(pl.a.vec && pl.b.vec);
     pl.ktiles = (int)cdiv(p.K, kel);
+    // The direct-to-LDS kernel serves whole 16-byte chunks and whole K tiles.
+    pl.dtl = !pl.slow && p.K % kel == 0 && !overrides().no_dtl;
     int tile = T64x64;
-    if (!pl.slow) {
+    int64_t S = 1;
+    if (pl.dtl) {
+        if (p.M <= 128) {
+            // Few rows: the shape is bound by streaming B, and the work is split
+            // over K to keep enough workgroups streaming.  Measured on MI355X
+            // (64x4096x4096 FP16, 128x7168x4096 FP8, 64x512x512): 64x64 tiles for
+            // 16-bit inputs and 64x128 for FP8 (twice the B bytes per K tile of
+            // A), each split holding at least 16 K tiles, up to about one
+            // workgroup per CU; each split adds a fixed cost (partials written,
+            // a ticket, partials read back by the last workgroup).
+            tile = p.fp8 ? T64x128 : T64x64;
+            if (p.M > 64 && !p.fp8 && tile_eff(p.M, p.N, T128x64) > tile_eff(p.M, p.N, tile) + 1e-9) tile = T128x64;
+            const int64_t nt = tile_count(p.M, p.N, tile);
+            S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 16));
+        } else {
+            // Enough rows for a compute-bound shape: the largest tile (FP8 stops at
+            // 128x128, whose promotion fits the registers) that still gives every
+            // CU a tile, else the one giving the most tiles; no split.
+            const int order[] = {T256x256, T128x128, T128x64, T64x64};
+            int64_t best_tiles = -1;
+            bool found = false;
+            for (int t : order) {
+                if (p.fp8 && t == T256x256) continue;
+                if (tile_eff(p.M, p.N, t) < 0.75 && t != T64x64) continue;
+                const int64_t nt = tile_count(p.M, p.N, t);
+                if (nt >= d.cus) { tile = t; found = true; break; }
+                if (nt > best_tiles) { best_tiles = nt; tile = t; }
+            }
+            (void)found;
+            const int64_t nt = tile_count(p.M, p.N, tile);
+            if (nt < d.cus && tile != T256x256 && tile != T128x128)
+                S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 8));
+        }
+        if (overrides().force_tile >= 0) tile = overrides().force_tile;
+    } else if (!pl.slow) {
+        // general kernel (register-staged loads, K tails): tiles it implements
         const int order[] = {T256x256, T128x128, T128x64, T64x64};
         int best = T64x64;
         int64_t best_tiles = -1;
         bool found = false;
         for (int t : order) {
-            // FP8 256x256: the per-K-block promotion of a 128x64 wave tile does not
-            // fit the registers of two waves per SIMD (it spills), so stop at 128
             if (p.fp8 && t == T256x256) continue;
-            const int64_t tm = cdiv(p.M, mfma_tile_bm(t)), tn = cdiv(p.N, mfma_tile_bn(t));
-            const int64_t nt = tm * tn;
-            // skip macro tiles that would be more than a quarter padding
-            const double eff = (double)p.M * (double)p.N /
-                               ((double)tm * mfma_tile_bm(t) * (double)tn * mfma_tile_bn(t));
-            if (eff < 0.75 && t != T64x64) continue;
+            if (tile_eff(p.M, p.N, t) < 0.75 && t != T64x64) continue;
+            const int64_t nt = tile_count(p.M, p.N, t);
             if (nt >= d.cus) { tile = t; found = true; break; }
             if (nt > best_tiles) { best_tiles = nt; best = t; }
         }
         if (!found) tile = best;
-        if (overrides().force_tile >= 0) tile = overrides().force_tile;
+        if (overrides().force_tile >= 0 && overrides().force_tile != T64x128) tile = overrides().force_tile;
+        const int64_t nt = tile_count(p.M, p.N, tile);
+        if (nt < d.cus) S = std::min<int64_t>(cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2));
+        S = std::min<int64_t>(S, 16);
     }
     pl.tile = tile;
     pl.tiles_m = (int)cdiv(p.M, mfma_tile_bm(tile));
     pl.tiles_n = (int)cdiv(p.N, mfma_tile_bn(tile));
-    const int64_t nt = (int64_t)pl.tiles_m * pl.tiles_n;
-    int64_t S = 1;
-    if (nt < d.cus) S = std::min<int64_t>(cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2));
-    S = std::min<int64_t>(S, 16);
     if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, std::max(pl.ktiles, 1));
+    // the direct kernel splits K only on tiles of at most 64 accumulators per lane
+    if (pl.dtl && (tile == T256x256)) S = 1;
     S = std::max<int64_t>(S, 1);
     pl.kt_per_split = (int)cdiv(std::max(pl.ktiles, 1), S);
     pl.splits = (int)cdiv(std::max(pl.ktiles, 1), pl.kt_per_split);
     pl.group_m = std::min(pl.tiles_m, 4);
     pl.lds_bytes = mfma_tile_lds(pl.slow ? T64x64 : tile, p.fp8);
-    pl.dtl = !pl.slow && mfma_dtl_tile(tile) && p.K % kel == 0 && !overrides().no_dtl;
+    pl.counters = pl.dtl && pl.splits > 1 ? pl.tiles_m * pl.tiles_n : 0;
 }
 
 }  // namespace
