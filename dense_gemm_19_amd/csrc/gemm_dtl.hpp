@@ -73,15 +73,15 @@ __device__ __forceinline__ int mnmaj_off(int k, int c) {
 // around it.  Every vector-memory instruction of the main loop is one of these,
 // so the kernel's counts are exact; any wait the compiler adds for its own
 // loads can only be stricter, since these are in-order counters.
-__device__ __forceinline__ void lds_load16(const void *g, const char *lds) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+__device__ __forceinline__ uint32_t lds_addr(const char *lds) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds;
+}
+// `a` is a wave-uniform LDS byte address (an SGPR); g is this lane's source.
+__device__ __forceinline__ void lds_load16(const void *g, uint32_t a) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void lds_load4(const void *g, const char *lds) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+__device__ __forceinline__ void lds_load4(const void *g, uint32_t a) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(a), "v"(g)
                  : "memory", "m0");
 }
@@ -96,8 +96,11 @@ struct DtlIO {
     static constexpr int CPR = R * EB / 16;         // chunks per K row (MNMAJ)
     static_assert(R * 8 % (64 * NW) == 0, "tile must split evenly over the waves");
 
-    // Issue the wave's loads of the tile whose first K element is k0 into lds.
-    __device__ static void issue(char *lds, const Operand &op, int r0, int k0, int Rlim, int wave, int lane) {
+    // This lane's source address for each of the wave's loads at K tile 0;
+    // tile kt adds kt * (K elements per tile) * k_stride, the same for every lane.
+    struct Src { const char *p[INSTS]; };
+    __device__ static Src sources(const Operand &op, int r0, int Rlim, int wave, int lane) {
+        Src s;
 #pragma unroll
         for (int j = 0; j < INSTS; ++j) {
             const int blk = wave + NW * j;            // 1 KB block of the tile
@@ -115,9 +118,16 @@ struct DtlIO {
             // rows past the edge read a real row (a whole in-range chunk for
             // MNMAJ, where a chunk spans EPC rows); their results are not stored
             const int gr = min(r0 + r, MODE == KMAJ ? Rlim - 1 : Rlim - EPC);
-            const char *src = op.ptr + (int64_t)gr * op.r_stride + (int64_t)(k0 + k) * op.k_stride;
-            lds_load16(src, lds + blk * 1024);
+            s.p[j] = op.ptr + (int64_t)gr * op.r_stride + (int64_t)k * op.k_stride;
         }
+        return s;
+    }
+
+    // Issue the wave's loads of the tile at byte offset koff along K into the
+    // LDS region at `lds` (wave-uniform address; wave_u the uniform wave index).
+    __device__ static void issue(uint32_t lds, const Src &s, int64_t koff, int wave_u) {
+#pragma unroll
+        for (int j = 0; j < INSTS; ++j) lds_load16(s.p[j] + koff, lds + (uint32_t)((wave_u + NW * j) * 1024));
     }
 };
 
@@ -146,20 +156,29 @@ __device__ __forceinline__ u32x4 frag16(const char *lds, int rb, int ks, int lan
     }
 }
 
+// 8-bit fragment (32 K values) of the 16 rows starting at rb.  The MFMA sums
+// over K, so any assignment of K values to (lane group, byte) serves as long as
+// A and B agree: lane group g = lane/16 takes K bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of the 128-byte tile, i.e. chunks g and g+4.  For a
+// K-contiguous operand the four groups then read chunks 0-3 (and 4-7) of their
+// rows together, the same conflict-free pattern as the 16-bit fragments.
 template <int MODE, int R>
 __device__ __forceinline__ i32x8 frag8(const char *lds, int rb, int lane) {
     i32x8 out;
+    const int s = lane & 15, g = lane >> 4;
     if (MODE == KMAJ) {
-        const int r = rb + (lane & 15), g = lane >> 4;
-        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, 2 * g));
-        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, 2 * g + 1));
+        const int r = rb + s;
+        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g));
+        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g + 4));
         out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
         out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
     } else {
-        const int s = lane & 15, g = lane >> 4;
+        // transpose reads: 8 consecutive K rows x 16 columns each, bytes 8q..8q+7
+        // of the fragment = K rows kb(q)..kb(q)+7
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int k = 32 * g + 8 * q + (s >> 1);
+            const int kb = (q < 2) ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2);
+            const int k = kb + (s >> 1);
             const int byte = rb + 8 * (s & 1);
             const int off = mnmaj_off<1, R>(k, byte >> 4) + (byte & 15);
             i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(as_lds<i32x2>(lds + off));
@@ -254,14 +273,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     const int sa_row = min(m0 + 64 * (wave % (F8 ? BM / 64 : 1)) + lane, p.M - 1);
     const int sb_blk = min((n0 >> 7) + lane, NBLK - 1);
 
-    auto fill = [&](char *st, int kt) __attribute__((always_inline)) {   // issue the loads of K tile kt into stage st
-        AIO::issue(st, p.a, m0, kt * KEL, p.M, wave, lane);
-        BIO::issue(st + A_BYTES, p.b, n0, kt * KEL, p.N, wave, lane);
+    // Source addresses are computed once; each tile only adds a uniform K offset.
+    // The LDS destinations are uniform too (the wave index, made uniform once).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const typename AIO::Src a_src = AIO::sources(p.a, m0, p.M, wave, lane);
+    const typename BIO::Src b_src = BIO::sources(p.b, n0, p.N, wave, lane);
+    const char *sa_src = F8 ? reinterpret_cast<const char *>(p.sa) + (int64_t)sa_row * p.sa_rs : nullptr;
+    const char *sb_src = F8 ? reinterpret_cast<const char *>(p.sb) + (int64_t)sb_blk * p.sb_cs : nullptr;
+    const int64_t a_kstep = (int64_t)KEL * p.a.k_stride, b_kstep = (int64_t)KEL * p.b.k_stride;
+    const uint32_t ring_lds = lds_addr(ring);
+
+    auto fill = [&](int stage_idx, int kt) __attribute__((always_inline)) {   // K tile kt into a stage
+        const uint32_t st = ring_lds + (uint32_t)(stage_idx * STAGE);
+        AIO::issue(st, a_src, kt * a_kstep, wave_u);
+        BIO::issue(st + A_BYTES, b_src, kt * b_kstep, wave_u);
         if constexpr (F8) {
-            const char *sa = reinterpret_cast<const char *>(p.sa) + (int64_t)sa_row * p.sa_rs + (int64_t)kt * p.sa_cs;
-            const char *sb = reinterpret_cast<const char *>(p.sb) + (int64_t)kt * p.sb_rs + (int64_t)sb_blk * p.sb_cs;
-            lds_load4(sa, st + SA_OFF + 256 * (wave % (BM / 64)));
-            lds_load4(sb, st + SB_OFF);
+            lds_load4(sa_src + (int64_t)kt * p.sa_cs, st + SA_OFF + 256 * (wave_u % (BM / 64)));
+            lds_load4(sb_src + (int64_t)kt * p.sb_rs, st + SB_OFF);
         }
     };
 
@@ -325,7 +353,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     // prologue: the first NS - 1 tiles go out
 #pragma unroll
     for (int q = 0; q + 1 < NS; ++q)
-        if (kt0 + q < kt1) fill(ring + q * STAGE, kt0 + q);
+        if (kt0 + q < kt1) fill(q, kt0 + q);
     // tile kt sits in stage `cur`; the stage freed by tile kt - 1 takes tile kt + NS - 1
     auto body = [&](int cur, int kt) __attribute__((always_inline)) {
         wait_tiles(min(NS - 2, kt1 - 1 - kt));
@@ -336,7 +364,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         // previous stage's reads have all been consumed by matrix instructions.
         asm volatile("s_barrier" ::: "memory");
         const int nxt = cur == 0 ? NS - 1 : cur - 1;
-        if (kt + NS - 1 < kt1) fill(ring + nxt * STAGE, kt + NS - 1);
+        if (kt + NS - 1 < kt1) fill(nxt, kt + NS - 1);
         compute(ring + cur * STAGE);
     };
     // (a rolled loop: unrolling it, even by two for NS = 2, pushes the 256x256
