@@ -52,6 +52,24 @@ __device__ __forceinline__ void store_out(char *p, int kind, float v) {
     else *reinterpret_cast<uint16_t *>(p) = f32_to_f16_bits(v);
 }
 
+// Sum of S split-K partials, ((p0 + p1) + p2) + ... always in this order, with
+// the loads issued 8 at a time so that their latencies overlap (a runtime-bounded
+// loop would otherwise wait for each load before issuing the next).
+// load(q) returns partial q.
+template <class Load>
+__device__ __forceinline__ float sum_partials(int S, Load load) {
+    float s = 0.f;
+    for (int q0 = 0; q0 < S; q0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = q0 + j < S ? load(q0 + j) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (q0 + j < S) s = q0 + j == 0 ? v[j] : s + v[j];
+    }
+    return s;
+}
+
 // out = alpha * acc + beta * C_in (C_in read only when beta != 0), rounded to the
 // C dtype and stored at (m, n).  The caller has checked m < M and n < N.
 __device__ __forceinline__ void epilogue_store(const Epilogue &e, int64_t m, int64_t n, float acc) {

@@ -18,8 +18,7 @@ __global__ void __launch_bounds__(NT) splitk_reduce(ReduceArgs p) {
     const int64_t total = (int64_t)p.M * p.N;
     const int64_t plane = total;
     for (int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * NT) {
-        float s = p.ws[idx];
-        for (int z = 1; z < p.S; ++z) s += p.ws[idx + z * plane];
+        const float s = sum_partials(p.S, [&](int z) { return p.ws[idx + z * plane]; });
         const int64_t m = idx / p.N, n = idx - m * p.N;
         epilogue_store(p.epi, m, n, s);
     }

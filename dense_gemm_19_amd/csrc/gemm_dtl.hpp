@@ -448,16 +448,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, mb + 16 * i + e, nb + 16 * j);
     for (int q = 1; q < p.splits; ++q) {
+        f32x4 v[TM][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {   // a 16-row block of partials at a time
-            f32x4 v[TN];
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[j][e] = part(q, mb + 16 * i + e, nb + 16 * j);
+                for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, mb + 16 * i + e, nb + 16 * j);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] += v[j];
-        }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] += v[i][j];
     }
     finish_any();
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

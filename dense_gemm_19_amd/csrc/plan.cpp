@@ -83,16 +83,17 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
     if (!no_vec && B.cols_contig() && B.cs == B.esize && B.align_ptr >= 16 && (p.K <= 1 || B.align_rs >= 16)) {
         pl.sk_kind = SK_BN;
         pl.sk_grid_x = (int)cdiv(p.N, SKINNY_BN_COLS);
-        // Split K until about two workgroups per CU stream B (the last one of a
-        // slab sums the partials), keeping at least one sweep per split.
-        int64_t S = std::max<int64_t>(1, std::min<int64_t>(cdiv(2LL * d.cus, pl.sk_grid_x),
-                                                           p.K / (2 * SKINNY_BN_SWEEP)));
-        if (overrides().force_splitk > 0) S = overrides().force_splitk;
-        S = std::max<int64_t>(1, std::min<int64_t>(S, std::max<int64_t>(1, p.K)));
-        // splits and LDS chunks are whole sweeps (only the last sweep of K is partial)
+        // Split K so that the grid fills the CUs without overfilling them: at
+        // most one workgroup per CU (a CU holding two would stream and multiply
+        // twice as much as the others and set the pace).  The splits are whole
+        // sweeps of as nearly equal length as the count allows (the last
+        // workgroup of a slab sums the partials), with at least two sweeps each.
         const int64_t sweep = SKINNY_BN_SWEEP;
-        int64_t kps = cdiv(std::max<int64_t>(p.K, 1), S);
-        kps = cdiv(kps, sweep) * sweep;
+        const int64_t sweeps = cdiv(std::max<int64_t>(p.K, 1), sweep);
+        int64_t S = std::max<int64_t>(1, std::min<int64_t>(d.cus / pl.sk_grid_x, sweeps / 2));
+        if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, sweeps);
+        // splits and LDS chunks are whole sweeps (only the last sweep of K is partial)
+        const int64_t kps = cdiv(sweeps, S) * sweep;
         pl.sk_k_per_split = (int)kps;
         pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
         pl.sk_mmax = mmax;

@@ -1,26 +1,27 @@
 // skinny.hip -- bandwidth-bound thin GEMM (M <= 8) without matrix cores.
 //
-// The pages single out thin shapes such as x[1,4096] . W1[4096,14336] (an MoE
+// The articles single out thin shapes such as x[1,4096] . W1[4096,14336] (an MoE
 // FFN up-projection) and q[1,4096] . K_cache^T (a 128-key cache): with M this
 // small the work is one pass over B, so the kernels stream B exactly once with
 // 16-byte loads, multiply on the vector ALUs, and reduce with cross-lane
 // shuffles and LDS instead of issuing matrix-core instructions ("DeepGEMM is
 // not a new model" article, cf-1.com, sections 2 and 4; sheratonhq.com deep
-// dive, section 5.4).  Stores are plain, one writer per output element, with
-// no atomics (cf-1.com article, section 4.5), so results are reproducible.
+// dive, section 5.4).  Every output element has one writer and partial sums
+// are added in a fixed order, never with floating-point atomics (cf-1.com
+// article, section 4.5), so results are reproducible.
 //
 // SK_BN: B is N-contiguous (row-major [K][N], e.g. W1).  A workgroup of 8 waves
-//   owns a slab of 64 columns (128 bytes of every row of B) and, unless K is
-//   split, all of K.  Lane (r, c) of a wave, r = lane/8, c = lane%8, owns
-//   columns 8c..8c+7 of the slab and, in each sweep, the U consecutive rows
-//   U*(8*wave + r) + u, u < U (U = 16 for M <= 2, else 8): each of its U loads
-//   is one 16-byte piece of a row, so every load instruction of a wave covers 8
-//   full 128-byte lines, and the A values a lane needs are 16-byte LDS reads.
-//   A lane issues its U loads, then multiplies; with 4 waves per SIMD the other
-//   waves' loads are in flight meanwhile (U*16 bytes per lane, 256 KB per CU
-//   for U = 16).  A's K slice is staged in LDS as 16-bit values [m][k].  The 8
-//   row groups of a wave are summed with shuffles and the 16 waves through LDS,
-//   always in the same order.
+//   owns a slab of 256 columns (512 bytes of every row of B) and one split of
+//   K.  Lane (r, c) of a wave, r = lane/32, c = lane%32, owns columns
+//   8c..8c+7 of the slab and, in each 128-row sweep, the 8 consecutive rows
+//   8*(2*wave + r) + u, u < 8: every load instruction of a wave reads two whole
+//   512-byte row pieces, and the A values a lane needs are 16-byte LDS reads.
+//   A's K slice is staged in LDS as 16-bit values [m][k], with the first
+//   sweep's loads of B already in flight.  The two row groups of a wave are
+//   summed with a shuffle and the 8 waves through LDS, always in the same
+//   order.  K is split so that the grid holds at most one workgroup per CU;
+//   the last workgroup of a slab to finish (an arrival counter) adds the S
+//   partials in the order s = 0..S-1, so the sum does not depend on timing.
 // SK_BK: B is K-contiguous (B = K_cache^T: column n is row n of the cache).  A
 //   wave owns one column; lanes take 8 consecutive K values each per 512-wide K
 //   step, with up to 8 steps' loads of B and A issued before any is used, then a
@@ -264,14 +265,15 @@ __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
                                          __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
     __syncthreads();
     if (!is_last) return;
+    const int64_t plane = (int64_t)p.M * p.N;
     for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
         const int m = t / BN_COLS, col = t - m * BN_COLS;
         const int n = blockIdx.x * BN_COLS + col;
         if (m < p.M && n < p.N) {
             float *w = p.ws + (int64_t)m * p.N + n;
-            float s = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int q = 1; q < p.splits; ++q)
-                s += __hip_atomic_load(w + (int64_t)q * p.M * p.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float s = sum_partials(p.splits, [&](int q) {
+                return __hip_atomic_load(w + q * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            });
             epilogue_store(p.epi, m, n, s);
         }
     }
