@@ -31,18 +31,27 @@
 namespace dg {
 namespace dtl {
 
-constexpr int KBYTES = 128;      // bytes of K per tile and row
-
+// A K tile carries KB bytes of K per row: 128 (the general case, and FP8,
+// whose matrix instruction consumes a whole 128-wide scale block), or 64 for
+// the largest 16-bit tile, which then fits four stages in LDS instead of two.
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int IN> struct InT;
-template <> struct InT<IN_F16>  { static constexpr int EB = 2; static constexpr int KSTEPS = 2; };
-template <> struct InT<IN_BF16> { static constexpr int EB = 2; static constexpr int KSTEPS = 2; };
-template <> struct InT<IN_F8>   { static constexpr int EB = 1; static constexpr int KSTEPS = 1; };
+template <> struct InT<IN_F16>  { static constexpr int EB = 2; };
+template <> struct InT<IN_BF16> { static constexpr int EB = 2; };
+template <> struct InT<IN_F8>   { static constexpr int EB = 1; };
 
 // ------------------------------------------------------------------ LDS layout (as gemm_mfma.hip)
 
-__device__ __forceinline__ int kmaj_off(int r, int c) { return r * KBYTES + ((c ^ (r & 7)) << 4); }
+// K-contiguous operands: row r holds KB/16 chunks of 16 bytes, XOR-swizzled so
+// that the 8 (or 16) rows one fragment read touches per LDS cycle, all at the
+// same logical chunk, fall on distinct banks.
+template <int KB>
+__device__ __forceinline__ int kmaj_swz(int r) {
+    return KB == 128 ? (r & 7) : (((r >> 1) ^ (r >> 3)) & 3);
+}
+template <int KB>
+__device__ __forceinline__ int kmaj_off(int r, int c) { return r * KB + ((c ^ kmaj_swz<KB>(r)) << 4); }
 
 // XOR swizzle of the 16-byte chunks of K row k (M/N-contiguous operands).  The
 // transpose reads of one 16-lane group touch 4 (16-bit) or 8 (8-bit) consecutive
@@ -76,29 +85,37 @@ __device__ __forceinline__ int mnmaj_off(int k, int c) {
 __device__ __forceinline__ uint32_t lds_addr(const char *lds) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds;
 }
-// `a` is a wave-uniform LDS byte address (an SGPR); g is this lane's source.
-__device__ __forceinline__ void lds_load16(const void *g, uint32_t a) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g)
+// `a` is a wave-uniform LDS byte address and `base` a wave-uniform global
+// address (both SGPRs); this lane's source is base + off.  The per-lane part is
+// a 32-bit offset that stays fixed over the K loop, so advancing a tile costs
+// one scalar add of the base and no vector instructions.
+__device__ __forceinline__ void lds_load16(const char *base, uint32_t off, uint32_t a) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a), "v"(off), "s"(base)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void lds_load4(const void *g, uint32_t a) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(a), "v"(g)
+__device__ __forceinline__ void lds_load4(const char *base, uint32_t off, uint32_t a) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(a), "v"(off), "s"(base)
                  : "memory", "m0");
 }
 
-// One operand's K tile: R rows (M for A, N for B) x 128 bytes of K, 8*R chunks
-// of 16 bytes, i.e. R/8 load instructions of a wave (64 chunks each), shared
-// by the NW waves.  Instruction j of wave w fills LDS bytes [1024*(w + NW*j), +1024).
-template <int MODE, int R, int EB, int NW>
+// One operand's K tile: R rows (M for A, N for B) x KB bytes of K, R*KB/16
+// chunks of 16 bytes, i.e. R*KB/1024 load instructions of a wave (64 chunks
+// each), shared by the NW waves.  Instruction j of wave w fills LDS bytes
+// [1024*(w + NW*j), +1024).
+template <int MODE, int R, int EB, int NW, int KB>
 struct DtlIO {
-    static constexpr int INSTS = R * 8 / 64 / NW;   // per wave
+    static constexpr int CR = KB / 16;              // chunks per row (KMAJ)
+    static constexpr int INSTS = R * CR / 64 / NW;  // per wave
     static constexpr int EPC = 16 / EB;             // elements per chunk
     static constexpr int CPR = R * EB / 16;         // chunks per K row (MNMAJ)
-    static_assert(R * 8 % (64 * NW) == 0, "tile must split evenly over the waves");
+    static_assert(R * CR % (64 * NW) == 0, "tile must split evenly over the waves");
 
-    // This lane's source address for each of the wave's loads at K tile 0;
-    // tile kt adds kt * (K elements per tile) * k_stride, the same for every lane.
-    struct Src { const char *p[INSTS]; };
+    // This lane's source for each of the wave's loads, as a byte offset from
+    // the tile origin (row r0 at K tile 0); K tile kt adds kt * (K elements per
+    // tile) * k_stride to the origin, the same for every lane.  The host keeps
+    // these offsets below 2^31 (rows clamp into [r0, Rlim): r0 < Rlim, and for
+    // M/N-contiguous operands Rlim is a multiple of EPC).
+    struct Src { uint32_t off[INSTS]; };
     __device__ static Src sources(const Operand &op, int r0, int Rlim, int wave, int lane) {
         Src s;
 #pragma unroll
@@ -107,9 +124,9 @@ struct DtlIO {
             const int pos = blk * 64 + lane;          // chunk position this lane fills
             int r, k;                                 // logical (row, K element) of that chunk
             if (MODE == KMAJ) {
-                const int row = pos >> 3, p = pos & 7;
+                const int row = pos / CR, p = pos % CR;
                 r = row;
-                k = ((p ^ (row & 7)) * EPC);
+                k = ((p ^ kmaj_swz<KB>(row)) * EPC);
             } else {
                 const int kk = pos / CPR, p = pos % CPR;
                 k = kk;
@@ -118,27 +135,27 @@ struct DtlIO {
             // rows past the edge read a real row (a whole in-range chunk for
             // MNMAJ, where a chunk spans EPC rows); their results are not stored
             const int gr = min(r0 + r, MODE == KMAJ ? Rlim - 1 : Rlim - EPC);
-            s.p[j] = op.ptr + (int64_t)gr * op.r_stride + (int64_t)k * op.k_stride;
+            s.off[j] = (uint32_t)((int64_t)(gr - r0) * op.r_stride + (int64_t)k * op.k_stride);
         }
         return s;
     }
 
-    // Issue the wave's loads of the tile at byte offset koff along K into the
-    // LDS region at `lds` (wave-uniform address; wave_u the uniform wave index).
-    __device__ static void issue(uint32_t lds, const Src &s, int64_t koff, int wave_u) {
+    // Issue the wave's loads of the tile whose origin is `base` (uniform) into
+    // the LDS region at `lds` (uniform; wave_u the uniform wave index).
+    __device__ static void issue(uint32_t lds, const Src &s, const char *base, int wave_u) {
 #pragma unroll
-        for (int j = 0; j < INSTS; ++j) lds_load16(s.p[j] + koff, lds + (uint32_t)((wave_u + NW * j) * 1024));
+        for (int j = 0; j < INSTS; ++j) lds_load16(base, s.off[j], lds + (uint32_t)((wave_u + NW * j) * 1024));
     }
 };
 
 // ------------------------------------------------------------------ fragments (as gemm_mfma.hip)
 
-template <int MODE, int R>
+template <int MODE, int R, int KB>
 __device__ __forceinline__ u32x4 frag16(const char *lds, int rb, int ks, int lane) {
     if (MODE == KMAJ) {
         const int r = rb + (lane & 15);
         const int c = ks * 4 + (lane >> 4);
-        return *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, c));
+        return *reinterpret_cast<const u32x4 *>(lds + kmaj_off<KB>(r, c));
     } else {
         const int s = lane & 15, g = lane >> 4;
         u32x4 out;
@@ -168,8 +185,8 @@ __device__ __forceinline__ i32x8 frag8(const char *lds, int rb, int lane) {
     const int s = lane & 15, g = lane >> 4;
     if (MODE == KMAJ) {
         const int r = rb + s;
-        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g));
-        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g + 4));
+        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off<128>(r, g));
+        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off<128>(r, g + 4));
         out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
         out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
     } else {
@@ -232,18 +249,20 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
 // sums the partials in the order s = 0..S-1, applies the epilogue, and re-arms
 // the counter (sheratonhq.com deep dive, section 5.2, with a fixed summation
 // order so that the bits do not depend on which workgroup finishes last).
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int KB>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int EB = InT<IN>::EB;
     constexpr bool F8 = (IN == IN_F8);
-    constexpr int A_BYTES = BM * KBYTES, B_BYTES = BN * KBYTES;
+    static_assert(KB == 128 || (KB == 64 && !F8), "K tile depth");
+    constexpr int KSTEPS = F8 ? 1 : KB / 64;     // 16-bit: matrix instructions of 32 K values
+    constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + (F8 ? BM * 4 : 0);
     constexpr int STAGE = SB_OFF + (F8 ? 256 : 0);
     constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 16, TN = WTN / 16;
-    constexpr int KEL = KBYTES / EB;
-    using AIO = DtlIO<AMODE, BM, EB, NW>;
-    using BIO = DtlIO<BMODE, BN, EB, NW>;
+    constexpr int KEL = KB / EB;
+    using AIO = DtlIO<AMODE, BM, EB, NW, KB>;
+    using BIO = DtlIO<BMODE, BN, EB, NW, KB>;
     constexpr int PER_FILL = AIO::INSTS + BIO::INSTS + (F8 ? 2 : 0);   // loads per wave per tile
     static_assert(NS >= 2 && NS <= 8, "2..8 stages");
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns lie in one 128-column scale block");
@@ -278,18 +297,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const typename AIO::Src a_src = AIO::sources(p.a, m0, p.M, wave, lane);
     const typename BIO::Src b_src = BIO::sources(p.b, n0, p.N, wave, lane);
-    const char *sa_src = F8 ? reinterpret_cast<const char *>(p.sa) + (int64_t)sa_row * p.sa_rs : nullptr;
-    const char *sb_src = F8 ? reinterpret_cast<const char *>(p.sb) + (int64_t)sb_blk * p.sb_cs : nullptr;
+    const uint32_t sa_off = F8 ? (uint32_t)((int64_t)sa_row * p.sa_rs) : 0u;
+    const uint32_t sb_off = F8 ? (uint32_t)((int64_t)sb_blk * p.sb_cs) : 0u;
+    const char *a_org = p.a.ptr + (int64_t)m0 * p.a.r_stride;
+    const char *b_org = p.b.ptr + (int64_t)n0 * p.b.r_stride;
     const int64_t a_kstep = (int64_t)KEL * p.a.k_stride, b_kstep = (int64_t)KEL * p.b.k_stride;
     const uint32_t ring_lds = lds_addr(ring);
 
     auto fill = [&](int stage_idx, int kt) __attribute__((always_inline)) {   // K tile kt into a stage
         const uint32_t st = ring_lds + (uint32_t)(stage_idx * STAGE);
-        AIO::issue(st, a_src, kt * a_kstep, wave_u);
-        BIO::issue(st + A_BYTES, b_src, kt * b_kstep, wave_u);
+        AIO::issue(st, a_src, a_org + kt * a_kstep, wave_u);
+        BIO::issue(st + A_BYTES, b_src, b_org + kt * b_kstep, wave_u);
         if constexpr (F8) {
-            lds_load4(sa_src + (int64_t)kt * p.sa_cs, st + SA_OFF + 256 * (wave_u % (BM / 64)));
-            lds_load4(sb_src + (int64_t)kt * p.sb_rs, st + SB_OFF);
+            lds_load4(reinterpret_cast<const char *>(p.sa) + (int64_t)kt * p.sa_cs, sa_off,
+                      st + SA_OFF + 256 * (wave_u % (BM / 64)));
+            lds_load4(reinterpret_cast<const char *>(p.sb) + (int64_t)kt * p.sb_rs, sb_off, st + SB_OFF);
         }
     };
 
@@ -317,19 +339,33 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
                 }
             }
         } else {
+            // The wave's B fragments of a K step stay in registers; A fragments
+            // are read one 16-row block at a time, PD blocks ahead of the matrix
+            // instructions that use them (a K step's B fragments with the first
+            // block of that step), so that each read's LDS latency hides behind
+            // the matrix instructions of the blocks before it.
+            constexpr int RA = AMODE == KMAJ ? 1 : 2, RB = BMODE == KMAJ ? 1 : 2;   // LDS reads per fragment
+            constexpr int STEPS = KSTEPS * TM, PD = 2;
+            u32x4 fb[KSTEPS][TN], fa[PD + 1];
+            auto read_step = [&](int t) __attribute__((always_inline)) {   // fragments of step t
+                const int ks = t / TM, i = t % TM;
+                if (i == 0) {
 #pragma unroll
-            for (int ks = 0; ks < InT<IN>::KSTEPS; ++ks) {
-                // the wave's B fragments of this K step stay in registers; A
-                // fragments are read one 16-row block at a time
-                u32x4 fb[TN];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) fb[j] = frag16<BMODE, BN>(lb, wn * WTN + 16 * j, ks, lane);
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const u32x4 fa = frag16<AMODE, BM>(la, wm * WTM + 16 * i, ks, lane);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<IN>(fa, fb[j], acc[i][j]);
+                    for (int j = 0; j < TN; ++j) fb[ks][j] = frag16<BMODE, BN, KB>(lb, wn * WTN + 16 * j, ks, lane);
+                    __builtin_amdgcn_sched_group_barrier(0x100, TN * RB, 0);
                 }
+                fa[t % (PD + 1)] = frag16<AMODE, BM, KB>(la, wm * WTM + 16 * i, ks, lane);
+                __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+            };
+#pragma unroll
+            for (int t = 0; t < PD && t < STEPS; ++t) read_step(t);
+#pragma unroll
+            for (int t = 0; t < STEPS; ++t) {
+                if (t + PD < STEPS) read_step(t + PD);
+                const int ks = t / TM, i = t % TM;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<IN>(fa[t % (PD + 1)], fb[ks][j], acc[i][j]);
+                __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
             }
         }
     };
@@ -360,19 +396,32 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         // A plain barrier: __syncthreads() would add a wait for every outstanding
         // load-to-LDS (they count as LDS writes), draining the ring.  This wave's
         // loads into tile kt are complete (wait above); the memory clobber keeps
-        // the compiler from moving LDS accesses or the refill across it; the
-        // previous stage's reads have all been consumed by matrix instructions.
-        asm volatile("s_barrier" ::: "memory");
+        // the compiler from moving LDS accesses or the refill across it, and the
+        // LDS wait before it completes this wave's reads of the stage that the
+        // refill below overwrites (the compiler may defer the matrix
+        // instructions that consume them past this point).
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int nxt = cur == 0 ? NS - 1 : cur - 1;
         if (kt + NS - 1 < kt1) fill(nxt, kt + NS - 1);
         compute(ring + cur * STAGE);
     };
-    // (a rolled loop: unrolling it, even by two for NS = 2, pushes the 256x256
-    // tile's 8-wave kernel past its 256 registers and it spills)
-    int cur = 0;
-    for (int kt = kt0; kt < kt1; ++kt) {
-        body(cur, kt);
-        cur = cur + 1 == NS ? 0 : cur + 1;
+    // With NS = 2 and 4 waves the loop runs two tiles per trip, so that each
+    // stage's LDS addresses are fixed offsets (immediates) rather than a
+    // per-trip vector add; the 256x256 tile's 8-wave kernel keeps a rolled loop
+    // (unrolled, it needs more than its 256 registers and spills).
+    if constexpr (NS == 2 && NW == 4) {
+        int kt = kt0;
+        for (; kt + 1 < kt1; kt += 2) {
+            body(0, kt);
+            body(1, kt + 1);
+        }
+        if (kt < kt1) body(0, kt);
+    } else {
+        int cur = 0;
+        for (int kt = kt0; kt < kt1; ++kt) {
+            body(cur, kt);
+            cur = cur + 1 == NS ? 0 : cur + 1;
+        }
     }
 
     // ---- epilogue: element (i, j, e) of a wave is C[mb + 16i + e][nb + 16j]
@@ -464,39 +513,49 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd>
-hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int KB>
+hipError_t launch_t(const MfmaArgs &args, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
+    // the host counts K tiles of 128 bytes; a 64-byte tile halves each one
+    MfmaArgs a = args;
+    if constexpr (KB == 64) {
+        a.ktiles *= 2;
+        a.kt_per_split *= 2;
+    }
     dim3 grid(a.tiles_m * a.tiles_n, 1, a.splits);
     if (a.splits > 1) {
         if constexpr (TM * TN <= 16) {
-            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true>), grid, dim3(64 * WGM * WGN), 0, s, a);
+            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true, KB>), grid, dim3(64 * WGM * WGN), 0, s, a);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;   // no split K for this tile (the planner never asks)
         }
     }
-    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false>), grid, dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, KB>), grid, dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int KB = 128>
 hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
-    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ>(a, s);
-    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ>(a, s);
-    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ>(a, s);
-    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ>(a, s);
+    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ, KB>(a, s);
+    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ, KB>(a, s);
+    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ, KB>(a, s);
+    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ, KB>(a, s);
 }
 
-// Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64 with 2
-// stages; 128x128 4 waves of 64x64 with 2 stages; the small tiles, used for
-// HBM-bound shapes with few rows, 4 waves with deep rings (6 or 8 stages), so
-// that enough bytes stream per CU to cover the memory latency (64x128 runs as
-// 1 x 4 waves of 64x32, so each stage carries twice as much of B as of A).
+// Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64, for
+// 16-bit inputs with four stages of 64 bytes of K (a stage's loads have three
+// tiles of compute to arrive in), for FP8 with two stages of 128; 128x128 4
+// waves of 64x64 with 2 stages (two workgroups share a CU); the small tiles,
+// used for HBM-bound shapes with few rows, 4 waves with deep rings (6 or 8
+// stages), so that enough bytes stream per CU to cover the memory latency
+// (64x128 runs as 1 x 4 waves of 64x32, so each stage carries twice as much of
+// B as of A).
 template <int IN>
 hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
     switch (tile) {
-    case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
+    case T256x256:
+        return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
     case T128x128: return launch_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, s);
     case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
     case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);

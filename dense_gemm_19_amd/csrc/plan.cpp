@@ -141,8 +141,15 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     if (overrides().no_vec) pl.a.vec = pl.b.vec = false;
     pl.slow = !(pl.a.vec && pl.b.vec);
     pl.ktiles = (int)cdiv(p.K, kel);
-    // The direct-to-LDS kernel serves whole 16-byte chunks and whole K tiles.
-    pl.dtl = !pl.slow && p.K % kel == 0 && !overrides().no_dtl;
+    // The direct-to-LDS kernel serves whole 16-byte chunks and whole K tiles,
+    // and addresses a lane's chunks with 32-bit offsets from the tile's first
+    // row (and the FP8 scales with 32-bit offsets from their K column): every
+    // such offset must stay below 2^31.
+    const int64_t lim = int64_t(1) << 31;
+    const bool a_fits = 255 * pl.a.r_stride + (kel - 1) * pl.a.k_stride + 16 < lim;
+    const bool b_fits = 255 * pl.b.r_stride + (kel - 1) * pl.b.k_stride + 16 < lim;
+    const bool s_fits = !p.fp8 || ((p.M - 1) * p.SA.rs + 4 < lim && (cdiv(p.N, 128) - 1) * p.SB.cs + 4 < lim);
+    pl.dtl = !pl.slow && p.K % kel == 0 && a_fits && b_fits && s_fits && !overrides().no_dtl;
     int tile = T64x64;
     int64_t S = 1;
     if (pl.dtl) {
