@@ -31,9 +31,8 @@
 namespace dg {
 namespace dtl {
 
-// A K tile carries KB bytes of K per row: 128 (the general case, and FP8,
-// whose matrix instruction consumes a whole 128-wide scale block), or 64 for
-// the largest 16-bit tile, which then fits four stages in LDS instead of two.
+constexpr int KB = 128;      // bytes of K per tile and row
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int IN> struct InT;
@@ -43,26 +42,23 @@ template <> struct InT<IN_F8>   { static constexpr int EB = 1; };
 
 // ------------------------------------------------------------------ LDS layout (as gemm_mfma.hip)
 
-// K-contiguous operands: row r holds KB/16 chunks of 16 bytes, XOR-swizzled so
-// that the 8 (or 16) rows one fragment read touches per LDS cycle, all at the
-// same logical chunk, fall on distinct banks.
-template <int KB>
-__device__ __forceinline__ int kmaj_swz(int r) {
-    return KB == 128 ? (r & 7) : (((r >> 1) ^ (r >> 3)) & 3);
-}
-template <int KB>
-__device__ __forceinline__ int kmaj_off(int r, int c) { return r * KB + ((c ^ kmaj_swz<KB>(r)) << 4); }
+// K-contiguous operands: row r holds 8 chunks of 16 bytes, XOR-swizzled so that
+// the 8 rows one fragment read touches per LDS cycle, all at the same logical
+// chunk, fall on distinct banks.
+__device__ __forceinline__ int kmaj_off(int r, int c) { return r * KB + ((c ^ (r & 7)) << 4); }
 
 // XOR swizzle of the 16-byte chunks of K row k (M/N-contiguous operands).  The
 // transpose reads of one 16-lane group touch 4 (16-bit) or 8 (8-bit) consecutive
-// K rows; the swizzle spreads those rows, and the K rows of the wave's other
-// lane groups (K bits 3-4 for 16-bit, 5-6 for 8-bit), over distinct banks.
+// K rows; the swizzle spreads those rows, and the K rows of the lane group read
+// in the same LDS cycle (K bits 3-4 for 16-bit; for 8-bit, bit 4, which tells
+// lane groups 0/1 and 2/3 of a read apart), over distinct banks.
 template <int EB, int CPR>
 __device__ __forceinline__ int mn_swz(int k) {
     int s;
     if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
     else if (CPR >= 32) s = (k & 7) | (((k >> 5) & 3) << 3);
-    else s = (k & 7) ^ ((k >> 5) & 3) ^ (CPR >= 16 ? ((k >> 5) & 1) << 3 : 0);
+    else if (CPR >= 16) s = (k & 7) ^ ((k >> 5) & 3) ^ (((k >> 5) & 1) << 3);
+    else s = (k & 7) ^ ((k >> 4) & 1);
     return s & (CPR - 1);
 }
 template <int EB, int R>
@@ -98,17 +94,15 @@ __device__ __forceinline__ void lds_load4(const char *base, uint32_t off, uint32
                  : "memory", "m0");
 }
 
-// One operand's K tile: R rows (M for A, N for B) x KB bytes of K, R*KB/16
-// chunks of 16 bytes, i.e. R*KB/1024 load instructions of a wave (64 chunks
-// each), shared by the NW waves.  Instruction j of wave w fills LDS bytes
-// [1024*(w + NW*j), +1024).
-template <int MODE, int R, int EB, int NW, int KB>
+// One operand's K tile: R rows (M for A, N for B) x 128 bytes of K, 8*R chunks
+// of 16 bytes, i.e. R/8 load instructions of a wave (64 chunks each), shared
+// by the NW waves.  Instruction j of wave w fills LDS bytes [1024*(w + NW*j), +1024).
+template <int MODE, int R, int EB, int NW>
 struct DtlIO {
-    static constexpr int CR = KB / 16;              // chunks per row (KMAJ)
-    static constexpr int INSTS = R * CR / 64 / NW;  // per wave
+    static constexpr int INSTS = R * 8 / 64 / NW;   // per wave
     static constexpr int EPC = 16 / EB;             // elements per chunk
     static constexpr int CPR = R * EB / 16;         // chunks per K row (MNMAJ)
-    static_assert(R * CR % (64 * NW) == 0, "tile must split evenly over the waves");
+    static_assert(R * 8 % (64 * NW) == 0, "tile must split evenly over the waves");
 
     // This lane's source for each of the wave's loads, as a byte offset from
     // the tile origin (row r0 at K tile 0); K tile kt adds kt * (K elements per
@@ -124,9 +118,9 @@ struct DtlIO {
             const int pos = blk * 64 + lane;          // chunk position this lane fills
             int r, k;                                 // logical (row, K element) of that chunk
             if (MODE == KMAJ) {
-                const int row = pos / CR, p = pos % CR;
+                const int row = pos >> 3, p = pos & 7;
                 r = row;
-                k = ((p ^ kmaj_swz<KB>(row)) * EPC);
+                k = ((p ^ (row & 7)) * EPC);
             } else {
                 const int kk = pos / CPR, p = pos % CPR;
                 k = kk;
@@ -150,12 +144,12 @@ struct DtlIO {
 
 // ------------------------------------------------------------------ fragments (as gemm_mfma.hip)
 
-template <int MODE, int R, int KB>
+template <int MODE, int R>
 __device__ __forceinline__ u32x4 frag16(const char *lds, int rb, int ks, int lane) {
     if (MODE == KMAJ) {
         const int r = rb + (lane & 15);
         const int c = ks * 4 + (lane >> 4);
-        return *reinterpret_cast<const u32x4 *>(lds + kmaj_off<KB>(r, c));
+        return *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, c));
     } else {
         const int s = lane & 15, g = lane >> 4;
         u32x4 out;
@@ -185,8 +179,8 @@ __device__ __forceinline__ i32x8 frag8(const char *lds, int rb, int lane) {
     const int s = lane & 15, g = lane >> 4;
     if (MODE == KMAJ) {
         const int r = rb + s;
-        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off<128>(r, g));
-        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off<128>(r, g + 4));
+        u32x4 lo = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g));
+        u32x4 hi = *reinterpret_cast<const u32x4 *>(lds + kmaj_off(r, g + 4));
         out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
         out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
     } else {
@@ -249,20 +243,19 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
 // sums the partials in the order s = 0..S-1, applies the epilogue, and re-arms
 // the counter (sheratonhq.com deep dive, section 5.2, with a fixed summation
 // order so that the bits do not depend on which workgroup finishes last).
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int KB>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int EB = InT<IN>::EB;
     constexpr bool F8 = (IN == IN_F8);
-    static_assert(KB == 128 || (KB == 64 && !F8), "K tile depth");
-    constexpr int KSTEPS = F8 ? 1 : KB / 64;     // 16-bit: matrix instructions of 32 K values
+    constexpr int KSTEPS = F8 ? 1 : 2;          // 16-bit: matrix instructions of 32 K values
     constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + (F8 ? BM * 4 : 0);
     constexpr int STAGE = SB_OFF + (F8 ? 256 : 0);
     constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 16, TN = WTN / 16;
     constexpr int KEL = KB / EB;
-    using AIO = DtlIO<AMODE, BM, EB, NW, KB>;
-    using BIO = DtlIO<BMODE, BN, EB, NW, KB>;
+    using AIO = DtlIO<AMODE, BM, EB, NW>;
+    using BIO = DtlIO<BMODE, BN, EB, NW>;
     constexpr int PER_FILL = AIO::INSTS + BIO::INSTS + (F8 ? 2 : 0);   // loads per wave per tile
     static_assert(NS >= 2 && NS <= 8, "2..8 stages");
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns lie in one 128-column scale block");
@@ -351,10 +344,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
                 const int ks = t / TM, i = t % TM;
                 if (i == 0) {
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) fb[ks][j] = frag16<BMODE, BN, KB>(lb, wn * WTN + 16 * j, ks, lane);
+                    for (int j = 0; j < TN; ++j) fb[ks][j] = frag16<BMODE, BN>(lb, wn * WTN + 16 * j, ks, lane);
                     __builtin_amdgcn_sched_group_barrier(0x100, TN * RB, 0);
                 }
-                fa[t % (PD + 1)] = frag16<AMODE, BM, KB>(la, wm * WTM + 16 * i, ks, lane);
+                fa[t % (PD + 1)] = frag16<AMODE, BM>(la, wm * WTM + 16 * i, ks, lane);
                 __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
             };
 #pragma unroll
@@ -496,66 +489,64 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, mb + 16 * i + e, nb + 16 * j);
+    // (IB 16-row blocks of a split at a time: at most 8 fragments of partials
+    // in registers beside the accumulators)
+    constexpr int IB = TM < (8 / TN > 0 ? 8 / TN : 1) ? TM : (8 / TN > 0 ? 8 / TN : 1);
     for (int q = 1; q < p.splits; ++q) {
-        f32x4 v[TM][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i0 = 0; i0 < TM; i0 += IB) {
+            f32x4 v[IB][TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int i = 0; i < IB; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, mb + 16 * i + e, nb + 16 * j);
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+                    for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, mb + 16 * (i0 + i) + e, nb + 16 * j);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] += v[i][j];
+            for (int i = 0; i < IB; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i0 + i][j] += v[i][j];
+        }
     }
     finish_any();
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int KB>
-hipError_t launch_t(const MfmaArgs &args, hipStream_t s) {
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd>
+hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
-    // the host counts K tiles of 128 bytes; a 64-byte tile halves each one
-    MfmaArgs a = args;
-    if constexpr (KB == 64) {
-        a.ktiles *= 2;
-        a.kt_per_split *= 2;
-    }
     dim3 grid(a.tiles_m * a.tiles_n, 1, a.splits);
     if (a.splits > 1) {
         if constexpr (TM * TN <= 16) {
-            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true, KB>), grid, dim3(64 * WGM * WGN), 0, s, a);
+            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true>), grid, dim3(64 * WGM * WGN), 0, s, a);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;   // no split K for this tile (the planner never asks)
         }
     }
-    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, KB>), grid, dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false>), grid, dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int KB = 128>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS>
 hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
-    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ, KB>(a, s);
-    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ, KB>(a, s);
-    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ, KB>(a, s);
-    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ, KB>(a, s);
+    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ>(a, s);
+    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ>(a, s);
+    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ>(a, s);
+    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ>(a, s);
 }
 
-// Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64, for
-// 16-bit inputs with four stages of 64 bytes of K (a stage's loads have three
-// tiles of compute to arrive in), for FP8 with two stages of 128; 128x128 4
-// waves of 64x64 with 2 stages (two workgroups share a CU); the small tiles,
-// used for HBM-bound shapes with few rows, 4 waves with deep rings (6 or 8
-// stages), so that enough bytes stream per CU to cover the memory latency
-// (64x128 runs as 1 x 4 waves of 64x32, so each stage carries twice as much of
-// B as of A).
+// Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64 with 2
+// stages (one workgroup per CU); 128x128 4 waves of 64x64 with 2 stages (two
+// workgroups share a CU, so that one's loads overlap the other's matrix
+// work); the small tiles, used for HBM-bound shapes with few rows, 4 waves
+// with deep rings (6 or 8 stages), so that enough bytes stream per CU to cover
+// the memory latency (64x128 runs as 1 x 4 waves of 64x32, so each stage
+// carries twice as much of B as of A).
 template <int IN>
 hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
     switch (tile) {
-    case T256x256:
-        return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
+    case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
     case T128x128: return launch_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, s);
     case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
     case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);

@@ -213,7 +213,9 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     S = std::max<int64_t>(S, 1);
     pl.kt_per_split = (int)cdiv(std::max(pl.ktiles, 1), S);
     pl.splits = (int)cdiv(std::max(pl.ktiles, 1), pl.kt_per_split);
-    pl.group_m = std::min(pl.tiles_m, 4);
+    // tile raster: a group of tile rows walked together (measured on the
+    // 4096-sized workloads: 4 rows of 256x256 tiles, 8 of 128x128)
+    pl.group_m = std::min(pl.tiles_m, tile == T128x128 ? 8 : 4);
     pl.lds_bytes = mfma_tile_lds(pl.slow ? T64x64 : tile, p.fp8);
     pl.counters = pl.dtl && pl.splits > 1 ? pl.tiles_m * pl.tiles_n : 0;
 }
