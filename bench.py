@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 dense GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs all|none|c1,c4,...]
-                    [--no-cpu] [--copy-calib]
+                    [--no-cpu] [--copy-calib] [--no-calib]
 
 One step is one pass of the thin-GEMM workload the pages single out: the BF16
 x.W1 up-projection of an MoE FFN, [1,4096] x [4096,14336], followed by the
@@ -20,6 +20,10 @@ The JSON line also carries:
                 HBM traffic read from rocprofv3 counters (profiles/), or null when
                 the kernel source changed since they were taken;
   cpu_baseline  the FP64 CPU oracle on the same step, on the host's cores;
+  measured_peaks  what this device sustains under ideal code, measured in the
+                same run (register-only MFMA loops, a 2 GiB streaming read, the
+                launch floor); roofline.frac_of_measured and each config's
+                frac_measured_* divide by these instead of the data-sheet peaks;
   configs       every other workload shape timed the same way (TFLOPS and the
                 fraction of the dense MFMA peak for M >= 64, GB/s and the
                 fraction of HBM peak for the thin and HBM-bound shapes).
@@ -217,6 +221,25 @@ def cpu_baseline(cases, budget_s=12.0):
                       f"FP64 arithmetic) in {t_total:.1f} s"}
 
 
+def measured_peaks(dg, nbytes=2 << 30):
+    """The denominators the hardware sustains under ideal code, measured now on
+    this device through the library's calibration entry points: register-only
+    matrix-instruction loops, a streaming read of 2 GiB (far above the 256 MB
+    last-level cache), and the back-to-back launch floor."""
+    import torch
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    torch.cuda.synchronize()
+    r = {"hbm_read_gbs": round(dg.calib_read(buf), 1),
+         "mfma_bf16_tflops": round(dg.calib_mfma(dg.DG_BF16), 1),
+         "mfma_fp8_tflops": round(dg.calib_mfma(dg.DG_F8E4M3), 1),
+         "launch_floor_us": round(dg.calib_launch(), 3),
+         "how": "register-only 16x16x32 BF16 / 16x16x128 FP8 MFMA loops on every CU; "
+                "16-byte nontemporal streaming read of 2 GiB; 2000 back-to-back empty launches"}
+    del buf
+    torch.cuda.empty_cache()
+    return r
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -240,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the measured peaks (register-only MFMA loops, 2 GiB read, launch floor)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X and has no "
@@ -323,6 +348,11 @@ def main():
     if args.copy_calib:
         copy_calibration()
 
+    measured = None
+    if not args.no_calib:
+        measured = measured_peaks(dg)
+        log("measured peaks:", json.dumps(measured))
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline([c2a, c2b])
@@ -343,8 +373,15 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": bytes_a,
                      "avg_launch_us": round(k_avg * 1e3, 3)},
         "cpu_baseline": cpu,
+        "measured_peaks": measured,
         "configs": others,
     }
+    if measured:
+        out["roofline"]["frac_of_measured"] = round(achieved / measured["hbm_read_gbs"], 4)
+        for n, r in others.items():
+            peak = measured["mfma_fp8_tflops"] if r["dtype"] == "fp8" else measured["mfma_bf16_tflops"]
+            r["frac_measured_mfma"] = round(r["tflops"] / peak, 4)
+            r["frac_measured_hbm"] = round(r["gbs"] / measured["hbm_read_gbs"], 4)
     print(json.dumps(out), flush=True)
 
 

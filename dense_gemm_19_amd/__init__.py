@@ -67,6 +67,12 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_char_p, ctypes.c_size_t]
         for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan"):
             getattr(L, f).restype = ctypes.c_int
+        D = ctypes.POINTER(ctypes.c_double)
+        L.dg_calib_mfma.argtypes = [ctypes.c_int, D, ctypes.c_void_p]
+        L.dg_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, D, ctypes.c_void_p]
+        L.dg_calib_launch.argtypes = [D, ctypes.c_void_p]
+        for f in ("dg_calib_mfma", "dg_calib_read", "dg_calib_launch"):
+            getattr(L, f).restype = ctypes.c_int
         L.dg_status_str.argtypes = [ctypes.c_int]
         L.dg_status_str.restype = ctypes.c_char_p
         L.dg_version.restype = ctypes.c_int
@@ -149,6 +155,30 @@ def plan(A, B, C, alpha: float = 1.0, beta: float = 0.0, A_scale=None, B_scale=N
                           None if B_scale is None else view_of(B_scale))
     _check(st, "dg_gemm_plan")
     return text
+
+
+# ---- measured roofline denominators (include/dg_calib.h)
+
+def calib_mfma(dtype: int, stream=None) -> float:
+    """Sustained dense matrix-instruction TFLOP/s (DG_BF16 or DG_F8E4M3)."""
+    out = ctypes.c_double(0.0)
+    _check(lib().dg_calib_mfma(dtype, ctypes.byref(out), _stream(stream)), "dg_calib_mfma")
+    return out.value
+
+
+def calib_read(buf: torch.Tensor, stream=None) -> float:
+    """Streaming read GB/s over a device tensor's bytes."""
+    out = ctypes.c_double(0.0)
+    _check(lib().dg_calib_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                               ctypes.byref(out), _stream(stream)), "dg_calib_read")
+    return out.value
+
+
+def calib_launch(stream=None) -> float:
+    """Back-to-back empty-kernel launch floor in microseconds."""
+    out = ctypes.c_double(0.0)
+    _check(lib().dg_calib_launch(ctypes.byref(out), _stream(stream)), "dg_calib_launch")
+    return out.value
 
 
 def status_str(st: int) -> str:

@@ -29,13 +29,13 @@ EXTRA_FLAGS = {"gemm_dtl_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 HIP_SOURCES = ["gemm_mfma.hip", "gemm_dtl_f16.hip", "gemm_dtl_bf16.hip", "gemm_dtl_f8.hip", "skinny.hip",
-               "epilogue.hip"]
+               "epilogue.hip", "calib.hip"]
 HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp", "gemm_dtl.cpp"]
 
 
 def _newest_header() -> float:
     hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
-    hs.append(os.path.join(ROOT, "include", "dg.h"))
+    hs += [os.path.join(ROOT, "include", h) for h in os.listdir(os.path.join(ROOT, "include"))]
     return max(os.path.getmtime(h) for h in hs)
 
 

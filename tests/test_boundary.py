@@ -16,14 +16,17 @@ BASE = 0x7F0000000000   # a fake, 256-byte aligned device address
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "dg.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dg_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dg_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan", "dg_status_str",
-            "dg_version"} <= set(names)
+            "dg_version", "dg_calib_mfma", "dg_calib_read", "dg_calib_launch"} <= set(names)
     L = dg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -199,3 +202,17 @@ def test_plans_for_the_workloads():
     assert field(p, "path") == "mfma" and int(field(p, "splits")) > 1
     p = dg.plan(t(4, 4, dt=torch.half), t(4, 4, dt=torch.half), t(4, 4, dt=torch.float32), 0.0, 1.0)
     assert field(p, "path") == "scale"
+
+
+def test_calib_argument_errors():
+    """The calibration entry points reject bad arguments before touching a device."""
+    import ctypes
+    L = dg.lib()
+    out = ctypes.c_double(0.0)
+    assert dg.STATUS[L.dg_calib_mfma(DG_F32, ctypes.byref(out), None)] == "DG_ERR_DTYPE"
+    assert dg.STATUS[L.dg_calib_mfma(DG_BF16, None, None)] == "DG_ERR_NULL"
+    assert dg.STATUS[L.dg_calib_read(None, 1024, ctypes.byref(out), None)] == "DG_ERR_NULL"
+    assert dg.STATUS[L.dg_calib_read(ctypes.c_void_p(BASE), 1000, ctypes.byref(out), None)] == "DG_ERR_MISALIGNED"
+    assert dg.STATUS[L.dg_calib_read(ctypes.c_void_p(BASE + 8), 1024, ctypes.byref(out), None)] == "DG_ERR_MISALIGNED"
+    assert dg.STATUS[L.dg_calib_read(ctypes.c_void_p(BASE), 0, ctypes.byref(out), None)] == "DG_ERR_MISALIGNED"
+    assert dg.STATUS[L.dg_calib_launch(None, None)] == "DG_ERR_NULL"
