@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_char_p, ctypes.c_size_t]
         for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan"):
             getattr(L, f).restype = ctypes.c_int
+        L.dg_quant_fp8.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p]
+        L.dg_quant_fp8.restype = ctypes.c_int
         D = ctypes.POINTER(ctypes.c_double)
         L.dg_calib_mfma.argtypes = [ctypes.c_int, D, ctypes.c_void_p]
         L.dg_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, D, ctypes.c_void_p]
@@ -155,6 +157,17 @@ def plan(A, B, C, alpha: float = 1.0, beta: float = 0.0, A_scale=None, B_scale=N
                           None if B_scale is None else view_of(B_scale))
     _check(st, "dg_gemm_plan")
     return text
+
+
+DG_QUANT_TOKEN, DG_QUANT_BLOCK = 0, 1
+
+
+def quant_fp8(X: torch.Tensor, Q: torch.Tensor, S: torch.Tensor, mode: int = DG_QUANT_TOKEN,
+              stream=None) -> None:
+    """Q, S <- FP8 E4M3 codes and FP32 scales of X (dg_quant_fp8)."""
+    vx, vq, vs = view_of(X), view_of(Q), view_of(S)
+    _check(lib().dg_quant_fp8(ctypes.byref(vx), ctypes.byref(vq), ctypes.byref(vs), mode, _stream(stream)),
+           "dg_quant_fp8")
 
 
 # ---- measured roofline denominators (include/dg_calib.h)

@@ -16,6 +16,7 @@
 #include "dg.h"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "quant.hpp"
 #include "view.hpp"
 
 namespace dg {
@@ -311,10 +312,57 @@ dg_status plan_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
     return DG_SUCCESS;
 }
 
+// FP8 quantizer (dg_quant_fp8): validate X, Q, S as include/dg.h states, then
+// launch one 256-thread workgroup per 128 x 128 tile of X.
+dg_status quant_entry(const dg_view *X, const dg_view *Q, const dg_view *S, int mode, hipStream_t stream) {
+    Mat x, q, sc;
+    dg_status st;
+    if ((st = canonicalize(X, &x)) != DG_SUCCESS) return st;
+    if ((st = canonicalize(Q, &q)) != DG_SUCCESS) return st;
+    if ((st = canonicalize(S, &sc)) != DG_SUCCESS) return st;
+    if (mode != DG_QUANT_TOKEN && mode != DG_QUANT_BLOCK) return DG_ERR_INVALID_ARG;
+    if (x.dtype != DG_F32 && x.dtype != DG_F16 && x.dtype != DG_BF16) return DG_ERR_DTYPE;
+    if (q.dtype != DG_F8E4M3 || sc.dtype != DG_F32) return DG_ERR_DTYPE;
+    const int64_t M = x.rows, K = x.cols;
+    if (q.rows != M || q.cols != K) return DG_ERR_SHAPE_MISMATCH;
+    const int64_t KB = cdiv(K, 128), MB = cdiv(M, 128);
+    if (sc.rows != (mode == DG_QUANT_TOKEN ? M : MB) || sc.cols != KB) return DG_ERR_SHAPE_MISMATCH;
+    if (M > INT32_MAX || K > INT32_MAX || MB * KB > INT32_MAX) return DG_ERR_OVERFLOW;
+    if (self_overlaps(q) || self_overlaps(sc)) return DG_ERR_STRIDE;
+    if (spans_overlap(q, x) || spans_overlap(sc, x) || spans_overlap(q, sc)) return DG_ERR_ALIAS;
+    if (M == 0 || K == 0) return DG_SUCCESS;
+    Device d;
+    if ((st = current_device(&d, true)) != DG_SUCCESS) return st;
+    if (!d.gfx950) return DG_ERR_ARCH;
+    if (env_on("DG_CHECK_POINTERS")) {
+        for (const Mat *m : {&x, &q, &sc})
+            if ((st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
+    }
+    QuantArgs a;
+    a.X = x.ptr; a.x_rs = x.rs; a.x_cs = x.cs;
+    a.Q = const_cast<char *>(q.ptr); a.q_rs = q.rs; a.q_cs = q.cs;
+    a.S = reinterpret_cast<float *>(const_cast<char *>(sc.ptr)); a.s_rs = sc.rs; a.s_cs = sc.cs;
+    a.M = (int)M; a.K = (int)K;
+    a.tiles_k = (int)KB;
+    a.block = mode == DG_QUANT_BLOCK;
+    a.x_vec = x.cols_contig() && x.cs == x.esize && x.align_ptr >= 16 && (M <= 1 || x.align_rs >= 16);
+    a.q_vec = q.cols_contig() && q.cs == 1 && q.align_ptr >= 8 && (M <= 1 || q.align_rs >= 8);
+    if (launch_quant(x.dtype, a, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_SUCCESS;
+}
+
 }  // namespace
 }  // namespace dg
 
 extern "C" {
+
+dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_quant_mode mode,
+                       hipStream_t stream) {
+    return dg::quant_entry(X, Q, S, (int)mode, stream);
+}
 
 dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,
                   hipStream_t stream) {

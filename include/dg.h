@@ -133,6 +133,36 @@ dg_status dg_gemm_fp8_plan(const dg_view *A, const dg_view *A_scale, const dg_vi
                            char *buf, size_t len);
 
 /* Static, human-readable name of a status code ("DG_ERR_ALIAS", ...). */
+/*
+ * FP8 E4M3 quantization of X, the producer of dg_gemm_fp8's operands: FP8 GEMM
+ * needs per-token or per-block FP32 scale factors that squeeze each block into
+ * the representable range, and a dedicated kernel applies them without an
+ * extra pass (sheratonhq.com deep dive, sections 2.4 and 5.4).  The blocks are
+ * those of dg_gemm_fp8's scale views: 1 x 128 (token) and 128 x 128.
+ *
+ *   X: M x K, DG_F32, DG_F16 or DG_BF16 (any strides; read only).
+ *   Q: M x K, DG_F8E4M3 (written; must not overlap itself, X or S).
+ *   S: FP32 scales (written; must not overlap itself, X or Q):
+ *        DG_QUANT_TOKEN  [M][ceil(K/128)]: one per row and 128-wide block of K
+ *                        (dg_gemm_fp8's A_scale when X is A);
+ *        DG_QUANT_BLOCK  [ceil(M/128)][ceil(K/128)]: one per 128x128 block
+ *                        (dg_gemm_fp8's B_scale when X is B as [K][N]).
+ * For each block, in FP32 with IEEE operations:
+ *   amax = max |x| over the block's elements (a partial block covers only the
+ *          elements inside X);
+ *   s    = max(amax, 1e-12) / 448;
+ *   q    = E4M3(min(max(x / s, -448), 448)), rounded to nearest, ties to an
+ *          even code; -0 keeps its sign.
+ * X must be finite: for a block holding NaN or Inf the codes and scale are
+ * unspecified (the call still completes).  M == 0 or K == 0: nothing happens.
+ * Same conventions as the GEMM entry points (asynchronous on `stream`, C
+ * untouched on error -- here Q and S).
+ */
+typedef enum { DG_QUANT_TOKEN = 0, DG_QUANT_BLOCK = 1 } dg_quant_mode;
+
+dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_quant_mode mode,
+                       hipStream_t stream);
+
 const char *dg_status_str(dg_status s);
 
 /* DG_VERSION of the built library. */

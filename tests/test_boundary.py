@@ -216,3 +216,27 @@ def test_calib_argument_errors():
     assert dg.STATUS[L.dg_calib_read(ctypes.c_void_p(BASE + 8), 1024, ctypes.byref(out), None)] == "DG_ERR_MISALIGNED"
     assert dg.STATUS[L.dg_calib_read(ctypes.c_void_p(BASE), 0, ctypes.byref(out), None)] == "DG_ERR_MISALIGNED"
     assert dg.STATUS[L.dg_calib_launch(None, None)] == "DG_ERR_NULL"
+
+
+def test_quant_validation():
+    """dg_quant_fp8 rejects bad views before touching a device (include/dg.h)."""
+    import ctypes
+    L = dg.lib()
+    M, K = 200, 300
+    X = mat(BASE, M, K, 2 * K, 2, DG_BF16)
+    Q = mat(BASE + 0x1000000, M, K, K, 1, DG_F8E4M3)
+    S_tok = mat(BASE + 0x2000000, M, 3, 12, 4, DG_F32)
+    S_blk = mat(BASE + 0x2000000, 2, 3, 12, 4, DG_F32)
+    q = lambda x, qq, ss, mode: dg.STATUS[L.dg_quant_fp8(ctypes.byref(x), ctypes.byref(qq), ctypes.byref(ss), mode, None)]
+    assert q(X, Q, S_blk, 0) == "DG_ERR_SHAPE_MISMATCH"          # token mode wants [M][3]
+    assert q(X, Q, S_tok, 1) == "DG_ERR_SHAPE_MISMATCH"          # block mode wants [2][3]
+    assert q(X, Q, S_tok, 2) == "DG_ERR_INVALID_ARG"
+    assert q(X, mat(BASE + 0x1000000, M, K, 2 * K, 2, DG_BF16), S_tok, 0) == "DG_ERR_DTYPE"
+    assert q(X, Q, mat(BASE + 0x2000000, M, 3, 6, 2, DG_BF16), 0) == "DG_ERR_DTYPE"
+    assert q(mat(BASE, M, K, K, 1, DG_F8E4M3), Q, S_tok, 0) == "DG_ERR_DTYPE"
+    assert q(X, mat(BASE + 0x1000000, M, K + 1, K + 1, 1, DG_F8E4M3), S_tok, 0) == "DG_ERR_SHAPE_MISMATCH"
+    assert q(X, mat(BASE + 64, M, K, K, 1, DG_F8E4M3), S_tok, 0) == "DG_ERR_ALIAS"          # Q inside X
+    assert q(X, Q, mat(BASE + 0x1000000 + 64, M, 3, 12, 4, DG_F32), 0) == "DG_ERR_ALIAS"   # S inside Q
+    assert q(X, mat(BASE + 0x1000000, M, K, 0, 1, DG_F8E4M3), S_tok, 0) == "DG_ERR_STRIDE"   # Q rows collide
+    Xe = mat(BASE, 0, K, 2 * K, 2, DG_BF16)
+    assert q(Xe, mat(BASE + 0x1000000, 0, K, K, 1, DG_F8E4M3), mat(BASE + 0x2000000, 0, 3, 12, 4, DG_F32), 0) == "DG_SUCCESS"
