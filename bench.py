@@ -26,7 +26,9 @@ The JSON line also carries:
                 frac_measured_* divide by these instead of the data-sheet peaks;
   configs       every other workload shape timed the same way (TFLOPS and the
                 fraction of the dense MFMA peak for M >= 64, GB/s and the
-                fraction of HBM peak for the thin and HBM-bound shapes).
+                fraction of HBM peak for the thin and HBM-bound shapes), and the
+                FP8 quantizer producing the FP8 GEMM's operands (q_a: A per
+                token, q_b: B per 128x128 block; GB/s against HBM peak).
 """
 from __future__ import annotations
 
@@ -122,6 +124,68 @@ def prepared(dg, sets):
     import torch
     stream = torch.cuda.current_stream().cuda_stream
     return [Call(dg, c, stream) for c in sets]
+
+
+class QuantCall:
+    """One prepared dg_quant_fp8 call (views built once)."""
+
+    def __init__(self, dg, x, q, sc, mode, stream):
+        import ctypes
+        self.views = [dg.view_of(t) for t in (x, q, sc)]
+        self.args = [ctypes.byref(v) for v in self.views] + [mode, stream]
+        self.fn = dg.lib().dg_quant_fp8
+        self.name = "dg_quant_fp8"
+
+    def __call__(self):
+        return self.fn(*self.args)
+
+
+# The FP8 workload's producers: its A operand quantized per token, its B
+# operand per 128x128 block, from BF16 N(0,1) sources (the same draws as the
+# quantizer's parity tests at these sizes).
+QUANT_CONFIGS = {"q_a": (4096, 4096, 0, 106), "q_b": (4096, 7168, 1, 107)}
+
+
+def time_quant(dg, name, trials=5):
+    """Per-launch time of dg_quant_fp8 on one workload over rotated buffer sets."""
+    import torch
+    import synth
+    M, K, mode, seed = QUANT_CONFIGS[name]
+    x0 = synth.to_dtype(synth.draw(synth.rng(seed), (M, K), "normal", 1.0), torch.bfloat16).to("cuda:0")
+    srows = M if mode == 0 else (M + 127) // 128
+    nsc = srows * ((K + 127) // 128)
+    per = M * K * 3 + nsc * 4
+    P = max(2, -(-CACHE_DEFEAT_BYTES // per))
+    stream = torch.cuda.current_stream().cuda_stream
+    sets = []
+    for _ in range(P):
+        x = x0.clone()
+        q = torch.empty(M, K, dtype=torch.float8_e4m3fn, device="cuda:0")
+        sc = torch.empty(srows, (K + 127) // 128, dtype=torch.float32, device="cuda:0")
+        sets.append((x, q, sc))
+    calls = [QuantCall(dg, x, q, sc, mode, stream) for x, q, sc in sets]
+    nbytes = M * K * 2 + M * K + nsc * 4
+    reps = max(20, min(2000, int(2e-3 / max(nbytes / 6e12, 2e-6))))
+    run_checked(calls, range(10))
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run_checked(calls, range(reps))
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    times.sort()
+    t = times[len(times) // 2]
+    gbs = nbytes / t / 1e9
+    del sets, calls
+    torch.cuda.empty_cache()
+    return {"us": round(t * 1e6, 3), "us_min": round(times[0] * 1e6, 3), "reps": reps, "buffer_sets": P,
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "dtype": "bf16->e4m3",
+            "shape": [M, K], "mode": "token 1x128" if mode == 0 else "block 128x128",
+            "path": "quant", "algorithmic_bytes": nbytes}
 
 
 def run_checked(calls, idx):
@@ -259,7 +323,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--configs", default="all",
-                    help="other workloads to time: all, none, or a comma list of c1,c3,c4,c5_128,c5_4096")
+                    help="other workloads to time: all, none, or a comma list of "
+                         "c1,c3,c4,c5_128,c5_4096 (GEMMs) and q_a,q_b (the FP8 quantizer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -340,9 +405,9 @@ def main():
     # ---- the other workloads
     others = {}
     names = [] if args.configs == "none" else (
-        ["c1", "c3", "c4", "c5_128", "c5_4096"] if args.configs == "all" else args.configs.split(","))
+        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b"] if args.configs == "all" else args.configs.split(","))
     for n in names:
-        others[n] = time_config(dg, n)
+        others[n] = time_quant(dg, n) if n in QUANT_CONFIGS else time_config(dg, n)
         log(n, json.dumps(others[n]))
 
     if args.copy_calib:
@@ -379,8 +444,9 @@ def main():
     if measured:
         out["roofline"]["frac_of_measured"] = round(achieved / measured["hbm_read_gbs"], 4)
         for n, r in others.items():
-            peak = measured["mfma_fp8_tflops"] if r["dtype"] == "fp8" else measured["mfma_bf16_tflops"]
-            r["frac_measured_mfma"] = round(r["tflops"] / peak, 4)
+            if "tflops" in r:
+                peak = measured["mfma_fp8_tflops"] if r["dtype"] == "fp8" else measured["mfma_bf16_tflops"]
+                r["frac_measured_mfma"] = round(r["tflops"] / peak, 4)
             r["frac_measured_hbm"] = round(r["gbs"] / measured["hbm_read_gbs"], 4)
     print(json.dumps(out), flush=True)
 

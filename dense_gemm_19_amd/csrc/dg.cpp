@@ -327,7 +327,7 @@ dg_status quant_entry(const dg_view *X, const dg_view *Q, const dg_view *S, int 
     if (q.rows != M || q.cols != K) return DG_ERR_SHAPE_MISMATCH;
     const int64_t KB = cdiv(K, 128), MB = cdiv(M, 128);
     if (sc.rows != (mode == DG_QUANT_TOKEN ? M : MB) || sc.cols != KB) return DG_ERR_SHAPE_MISMATCH;
-    if (M > INT32_MAX || K > INT32_MAX || MB * KB > INT32_MAX) return DG_ERR_OVERFLOW;
+    if (M > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * KB > INT32_MAX / 2) return DG_ERR_OVERFLOW;
     if (self_overlaps(q) || self_overlaps(sc)) return DG_ERR_STRIDE;
     if (spans_overlap(q, x) || spans_overlap(sc, x) || spans_overlap(q, sc)) return DG_ERR_ALIAS;
     if (M == 0 || K == 0) return DG_SUCCESS;
@@ -347,7 +347,7 @@ dg_status quant_entry(const dg_view *X, const dg_view *Q, const dg_view *S, int 
     a.block = mode == DG_QUANT_BLOCK;
     a.x_vec = x.cols_contig() && x.cs == x.esize && x.align_ptr >= 16 && (M <= 1 || x.align_rs >= 16);
     a.q_vec = q.cols_contig() && q.cs == 1 && q.align_ptr >= 8 && (M <= 1 || q.align_rs >= 8);
-    if (launch_quant(x.dtype, a, stream) != hipSuccess) {
+    if (launch_quant(x.dtype, a, stream, d.cus) != hipSuccess) {
         (void)hipGetLastError();
         return DG_ERR_HIP;
     }

@@ -3,11 +3,12 @@
 // nearest with ties to an even code (include/dg.h states the operation and
 // cites the pages).
 //
-// One workgroup of 256 threads owns a 128 x 128 tile of X.  Thread t holds the
-// 8-element chunk cc = t % 16 of rows r0 + 16 i, r0 = t / 16, i < 8, so the 16
-// lanes of a row block are adjacent: the row maxima come from four shuffle
-// steps, the tile maximum from two more and one LDS exchange between the four
-// waves.  X is read once (16-byte loads where rows are K-contiguous) and the
+// One workgroup of 256 threads owns a 128 x 128 tile of X for block scales, or
+// a 64 x 128 tile for token scales (more, smaller workgroups: the loads of
+// later ones overlap the arithmetic of earlier ones).  Thread t holds the
+// 8-element chunk cc = t % 16 of rows r0 + 16 i, r0 = t / 16, so the 16 lanes
+// of a row block are adjacent: the row maxima come from four shuffle steps,
+// the tile maximum from two more and one LDS exchange between the four waves.  X is read once (16-byte loads where rows are K-contiguous) and the
 // codes of a chunk leave as one 8-byte store.  The work is a stream: 3 bytes
 // per element for 16-bit X, 5 for FP32.
 #include "dg.h"
@@ -19,95 +20,104 @@ namespace {
 
 constexpr float E4M3_MAX = 448.0f;
 
-// E4M3FN code of a finite v with |v| <= 448 (OCP FP8: bias 7, 3 mantissa
-// bits, subnormals m * 2^-9, largest finite 448 = 1.75 * 2^8), rounded to
-// nearest with ties to even.  Below 2^-6 the value is a multiple of 2^-9;
-// above, a 3-bit mantissa at the value's binary exponent.  Scaling by powers
-// of two is exact, so the only rounding is the one rint does (ties to even).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    uint32_t code;
-    if (a < 0.015625f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8; 8 is 2^-6, code 0x08
-    } else {
-        int e;
-        (void)__builtin_frexpf(a, &e);                  // a = f * 2^e, f in [0.5, 1)
-        int ex = e - 1;                                 // a in [2^ex, 2^(ex+1)), ex in [-6, 8]
-        uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - ex));   // 8..16
-        if (m == 16u) {
-            m = 8u;
-            ex += 1;
-        }
-        code = ((uint32_t)(ex + 7) << 3) | (m - 8u);
-    }
-    return sign | code;
+// x / s rounded to nearest, given r = RN(1/s): t = RN(x * r) is within one ulp
+// of the quotient, the FMA residual x - t * s is exact, and one correction
+// t + residual * r rounds to the correctly rounded quotient (Markstein's
+// theorem).  Here |x / s| <= 448 (s is the block's amax / 448), so nothing
+// overflows; where the quotient would be subnormal, i.e. far below the
+// smallest E4M3 step, any residual error cannot change the code.  The sign is
+// that of x (s > 0): the correction of x = -0 would otherwise give +0.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+    const float t = x * r;
+    const float e = fmaf(-t, s, x);
+    return __builtin_copysignf(fmaf(e, r, t), x);
+}
+
+// E4M3FN codes (OCP FP8: bias 7, 3 mantissa bits, subnormals m * 2^-9,
+// largest finite 448) of four finite values with |v| <= 448, rounded to
+// nearest with ties to even: gfx950's packed FP32 -> FP8 conversion, which
+// produces exactly these codes (it matched an arithmetic encoder on 7.6 M
+// values from 2^-20 to 448, and the parity tests check every E4M3 midpoint).
+// Byte j of the result is the code of v[j].
+__device__ __forceinline__ uint32_t e4m3_codes4(float v0, float v1, float v2, float v3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    return (uint32_t)w;
+}
+
+// An 8-element chunk of X as raw 32-bit words: 8 FP32 values, or 4 pairs of
+// 16-bit values (low half first).
+template <int XT> struct Chunk { static constexpr int W = XT == DG_F32 ? 8 : 4; uint32_t w[W]; };
+
+template <int XT>
+__device__ __forceinline__ uint32_t load_bits(const char *p) {
+    if (XT == DG_F32) return *reinterpret_cast<const uint32_t *>(p);
+    return *reinterpret_cast<const uint16_t *>(p);
 }
 
 template <int XT>
-__device__ __forceinline__ float load_x(const char *p) {
-    if (XT == DG_F32) return *reinterpret_cast<const float *>(p);
-    const uint16_t b = *reinterpret_cast<const uint16_t *>(p);
-    return XT == DG_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+__device__ __forceinline__ float chunk_value(const Chunk<XT> &c, int j) {
+    if (XT == DG_F32) return __builtin_bit_cast(float, c.w[j]);
+    const uint16_t h = (uint16_t)(j & 1 ? c.w[j >> 1] >> 16 : c.w[j >> 1] & 0xffffu);
+    return XT == DG_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
 }
 
-template <int XT>
-__global__ void __launch_bounds__(256) quant_fp8(QuantArgs p) {
-    __shared__ float wave_max[4];
-    const int t = threadIdx.x, cc = t & 15, r0 = t >> 4;
-    const int mb = blockIdx.x / p.tiles_k, kb = blockIdx.x - mb * p.tiles_k;
+// The thread's RT chunks of tile `tile`: rows r0 + 16 i of the tile's 16*RT rows,
+// columns 8 cc .. 8 cc + 7 of its 128; zeros outside X.
+template <int XT, int RT>
+__device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, int cc, Chunk<XT> (&buf)[RT]) {
+    const int mb = tile / p.tiles_k, kb = tile - mb * p.tiles_k;
     const int c0 = kb * 128 + cc * 8;
-    const int nvalid = min(8, p.K - c0);   // columns of this chunk inside X (may be <= 0)
-
-    float v[8][8];
+    const int nvalid = min(8, p.K - c0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = mb * 128 + r0 + 16 * i;
+    for (int i = 0; i < RT; ++i) {
+        const int row = mb * 16 * RT + r0 + 16 * i;
         const char *xr = p.X + (int64_t)row * p.x_rs;
         if (row < p.M && nvalid == 8 && p.x_vec) {
-            if (XT == DG_F32) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + (int64_t)c0 * 4);
-                const u32x4 b = *reinterpret_cast<const u32x4 *>(xr + (int64_t)c0 * 4 + 16);
+#pragma unroll
+            for (int h = 0; h < Chunk<XT>::W / 4; ++h) {
+                const u32x4 q = *reinterpret_cast<const u32x4 *>(xr + (int64_t)c0 * (XT == DG_F32 ? 4 : 2) + 16 * h);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    // (copy each vector element to a scalar first: a bit cast of
-                    // the element expression itself reads element 0 here)
-                    const uint32_t wa = a[j], wb = b[j];
-                    v[i][j] = __builtin_bit_cast(float, wa);
-                    v[i][4 + j] = __builtin_bit_cast(float, wb);
-                }
-            } else {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + (int64_t)c0 * 2);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint16_t lo = (uint16_t)(a[j] & 0xffffu), hi = (uint16_t)(a[j] >> 16);
-                    v[i][2 * j] = XT == DG_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
-                    v[i][2 * j + 1] = XT == DG_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+                    const uint32_t w = q[j];   // (an element copied to a scalar before any bit cast)
+                    buf[i].w[4 * h + j] = w;
                 }
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[i][j] = (row < p.M && j < nvalid) ? load_x<XT>(xr + (int64_t)(c0 + j) * p.x_cs) : 0.0f;
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t b = (row < p.M && j < nvalid) ? load_bits<XT>(xr + (int64_t)(c0 + j) * p.x_cs) : 0u;
+                if (XT == DG_F32) buf[i].w[j] = b;
+                else if (j & 1) buf[i].w[j >> 1] |= b << 16;
+                else buf[i].w[j >> 1] = b;
+            }
         }
     }
+}
 
+// Quantize one tile from the thread's chunks: row maxima, scales, codes, stores.
+template <int XT, int RT>
+__device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, int r0, int cc,
+                                           const Chunk<XT> (&buf)[RT], float *wave_max) {
+    const int mb = tile / p.tiles_k, kb = tile - mb * p.tiles_k;
+    const int c0 = kb * 128 + cc * 8;
+    const int nvalid = min(8, p.K - c0);
     // row maxima over the 16 lanes of each row block (out-of-range elements are 0)
-    float s[8];
+    float s[RT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RT; ++i) {
         float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[i][j]));
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(chunk_value<XT>(buf[i], j)));
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
         s[i] = a;
     }
     if (!p.block) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RT; ++i) {
             s[i] = fmaxf(s[i], 1e-12f) / E4M3_MAX;
-            const int row = mb * 128 + r0 + 16 * i;
+            const int row = mb * 16 * RT + r0 + 16 * i;
             if (cc == 0 && row < p.M)
                 *reinterpret_cast<float *>(reinterpret_cast<char *>(p.S) + (int64_t)row * p.s_rs +
                                            (int64_t)kb * p.s_cs) = s[i];
@@ -115,7 +125,7 @@ __global__ void __launch_bounds__(256) quant_fp8(QuantArgs p) {
     } else {
         float a = s[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) a = fmaxf(a, s[i]);
+        for (int i = 1; i < RT; ++i) a = fmaxf(a, s[i]);
         a = fmaxf(a, __shfl_xor(a, 16));
         a = fmaxf(a, __shfl_xor(a, 32));
         if ((t & 63) == 0) wave_max[t >> 6] = a;
@@ -123,39 +133,75 @@ __global__ void __launch_bounds__(256) quant_fp8(QuantArgs p) {
         a = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
         const float sc = fmaxf(a, 1e-12f) / E4M3_MAX;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s[i] = sc;
+        for (int i = 0; i < RT; ++i) s[i] = sc;
         if (t == 0)
             *reinterpret_cast<float *>(reinterpret_cast<char *>(p.S) + (int64_t)mb * p.s_rs +
                                        (int64_t)kb * p.s_cs) = sc;
     }
-
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = mb * 128 + r0 + 16 * i;
+    for (int i = 0; i < RT; ++i) {
+        const int row = mb * 16 * RT + r0 + 16 * i;
         if (row >= p.M || nvalid <= 0) continue;
-        uint32_t code[8];
+        const float r = 1.0f / s[i];
+        float c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) code[j] = e4m3_code(fminf(fmaxf(v[i][j] / s[i], -E4M3_MAX), E4M3_MAX));
+        for (int j = 0; j < 8; ++j)
+            c[j] = fminf(fmaxf(div_by_scale(chunk_value<XT>(buf[i], j), s[i], r), -E4M3_MAX), E4M3_MAX);
+        const uint32_t lo = e4m3_codes4(c[0], c[1], c[2], c[3]);
+        const uint32_t hi = e4m3_codes4(c[4], c[5], c[6], c[7]);
         char *qr = p.Q + (int64_t)row * p.q_rs;
         if (nvalid == 8 && p.q_vec) {
-            const uint32_t lo = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-            const uint32_t hi = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
             *reinterpret_cast<uint64_t *>(qr + c0) = (uint64_t)lo | ((uint64_t)hi << 32);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (j < nvalid) *reinterpret_cast<uint8_t *>(qr + (int64_t)(c0 + j) * p.q_cs) = (uint8_t)code[j];
+                if (j < nvalid)
+                    *reinterpret_cast<uint8_t *>(qr + (int64_t)(c0 + j) * p.q_cs) =
+                        (uint8_t)((j < 4 ? lo : hi) >> (8 * (j & 3)));
         }
+    }
+}
+
+// RT: 16-row groups per thread (8: 128 x 128 tiles; 4: 64 x 128, token scales
+// only).  Each workgroup walks tiles bid, bid + grid, ... with the next tile's
+// loads in flight while it quantizes and stores the current one, so that the
+// reads and writes of the whole grid overlap instead of running in two waves.
+template <int XT, int RT>
+__global__ void __launch_bounds__(256) quant_fp8(QuantArgs p, int ntiles) {
+    __shared__ float wave_max[2][4];   // (double-buffered: the next tile writes the other half)
+    const int t = threadIdx.x, cc = t & 15, r0 = t >> 4;
+    Chunk<XT> b0[RT], b1[RT];
+    int tile = blockIdx.x;
+    if (tile < ntiles) load_tile<XT, RT>(p, tile, r0, cc, b0);
+    for (; tile < ntiles; tile += 2 * gridDim.x) {
+        const int t1 = tile + gridDim.x, t2 = t1 + gridDim.x;
+        if (t1 < ntiles) load_tile<XT, RT>(p, t1, r0, cc, b1);
+        quant_tile<XT, RT>(p, tile, t, r0, cc, b0, wave_max[0]);
+        if (t1 >= ntiles) break;
+        if (t2 < ntiles) load_tile<XT, RT>(p, t2, r0, cc, b0);
+        quant_tile<XT, RT>(p, t1, t, r0, cc, b1, wave_max[1]);
     }
 }
 
 }  // namespace
 
-hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)((a.M + 127) / 128) * a.tiles_k)), block(256);
-    if (x_dtype == DG_F32) hipLaunchKernelGGL(quant_fp8<DG_F32>, grid, block, 0, stream, a);
-    else if (x_dtype == DG_F16) hipLaunchKernelGGL(quant_fp8<DG_F16>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(quant_fp8<DG_BF16>, grid, block, 0, stream, a);
+hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream, int cus) {
+    // Token scales: 64 x 128 tiles; block scales need the whole 128 x 128 block
+    // in one workgroup.  A persistent grid of 2 workgroups per CU walks them.
+    const int rows = a.block ? 128 : 64;
+    const int64_t ntiles = (int64_t)((a.M + rows - 1) / rows) * a.tiles_k;
+    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * (a.block ? 3 : 4);
+    const dim3 grid((unsigned)(ntiles < want ? ntiles : want)), block(256);
+    const int n = (int)ntiles;
+    if (a.block) {
+        if (x_dtype == DG_F32) hipLaunchKernelGGL((quant_fp8<DG_F32, 8>), grid, block, 0, stream, a, n);
+        else if (x_dtype == DG_F16) hipLaunchKernelGGL((quant_fp8<DG_F16, 8>), grid, block, 0, stream, a, n);
+        else hipLaunchKernelGGL((quant_fp8<DG_BF16, 8>), grid, block, 0, stream, a, n);
+    } else {
+        if (x_dtype == DG_F32) hipLaunchKernelGGL((quant_fp8<DG_F32, 4>), grid, block, 0, stream, a, n);
+        else if (x_dtype == DG_F16) hipLaunchKernelGGL((quant_fp8<DG_F16, 4>), grid, block, 0, stream, a, n);
+        else hipLaunchKernelGGL((quant_fp8<DG_BF16, 4>), grid, block, 0, stream, a, n);
+    }
     return hipGetLastError();
 }
 

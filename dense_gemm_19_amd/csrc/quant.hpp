@@ -17,7 +17,8 @@ struct QuantArgs {
     int q_vec;                           // Q rows K-contiguous, 8-byte aligned 8-element chunks
 };
 
-// x_dtype: DG_F32, DG_F16 or DG_BF16.
-hipError_t launch_quant(int x_dtype, const QuantArgs &args, hipStream_t stream);
+// x_dtype: DG_F32, DG_F16 or DG_BF16; cus: compute units of the device (sizes
+// the persistent grid).
+hipError_t launch_quant(int x_dtype, const QuantArgs &args, hipStream_t stream, int cus);
 
 }  // namespace dg

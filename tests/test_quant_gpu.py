@@ -84,6 +84,25 @@ def test_special_values(dg):
         check(dg, x, mode)
 
 
+def test_every_e4m3_midpoint(dg):
+    # a block holding 448 has s = 448 / 448 = 1 exactly, so x / s = x: put every
+    # midpoint between adjacent E4M3 values, and the FP32 values on either side
+    # of it, through the kernel's rounding (ties go to the even code)
+    vals = [oq.e4m3_value(c) for c in range(0x7F)]
+    mids = np.array([(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])], dtype=np.float32)
+    pts = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(448))])
+    pts = np.concatenate([pts, -pts]).astype(np.float32)
+    rows = -(-pts.size // 127)
+    body = np.zeros(rows * 127, dtype=np.float32)
+    body[: pts.size] = pts
+    x = np.zeros((rows, 128), dtype=np.float32)
+    x[:, :127] = body.reshape(rows, 127)
+    x[:, 127] = 448.0   # every row block holds 448: s = 1 per token and per block
+    assert np.isin(pts, x).all()
+    check(dg, torch.from_numpy(x), TOKEN)
+    check(dg, torch.from_numpy(x), BLOCK)
+
+
 @pytest.mark.parametrize("which", ["a_token_4096x4096", "b_block_4096x7168"])
 def test_workload_sizes(dg, which):
     # the producers of the 4096x7168x4096 FP8 GEMM's operands, at full size
