@@ -93,12 +93,15 @@ def _round_to(x: np.ndarray, fmt: str) -> np.ndarray:
 
 def compare(C_gpu, ref, out_fmt: str, rtol: float, literal: bool = False) -> CompareReport:
     """Compare GPU rows `ref.rows` of C against the reference element by element."""
+    return _report(C_gpu, ref.C, bound(ref, out_fmt, rtol, literal), ref.rows, out_fmt)
+
+
+def _report(C_gpu, want: np.ndarray, b: np.ndarray, rows, out_fmt: str) -> CompareReport:
+    """Report of |C_gpu - want| against the per-element bound b (rows: row ids of want)."""
     if isinstance(C_gpu, torch.Tensor):
         C_gpu = C_gpu.detach().to("cpu", torch.float64).numpy()
     got = np.asarray(C_gpu, dtype=np.float64)
-    want = ref.C
     assert got.shape == want.shape, (got.shape, want.shape)
-    b = bound(ref, out_fmt, rtol, literal)
     nan_g, nan_w = np.isnan(got), np.isnan(want)
     nan_mismatch = int(np.count_nonzero(nan_g != nan_w))
     both = ~(nan_g | nan_w)
@@ -111,7 +114,7 @@ def compare(C_gpu, ref, out_fmt: str, rtol: float, literal: bool = False) -> Com
     if ratio.size:
         idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
         mx = float(ratio[idx])
-        argmax = (int(ref.rows[idx[0]]), int(idx[1]))
+        argmax = (int(rows[idx[0]]), int(idx[1]))
     else:
         mx, argmax = 0.0, (-1, -1)
     nb = max(int(np.count_nonzero(both)), 1)
