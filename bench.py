@@ -26,9 +26,12 @@ The JSON line also carries:
                 frac_measured_* divide by these instead of the data-sheet peaks;
   configs       every other workload shape timed the same way (TFLOPS and the
                 fraction of the dense MFMA peak for M >= 64, GB/s and the
-                fraction of HBM peak for the thin and HBM-bound shapes), and the
+                fraction of HBM peak for the thin and HBM-bound shapes), the
                 FP8 quantizer producing the FP8 GEMM's operands (q_a: A per
-                token, q_b: B per 128x128 block; GB/s against HBM peak).
+                token, q_b: B per 128x128 block; GB/s against HBM peak), and
+                the fused bias + GELU epilogue on three of the GEMMs (*_gelu:
+                vs_plain_us is its cost over the plain GEMM, unfused_floor_us
+                the least a separate bias + GELU pass over C would take).
 """
 from __future__ import annotations
 
@@ -64,6 +67,8 @@ def algorithmic(case):
     M, N, K = case.mnk
     es = lambda t: t.element_size()
     b = M * K * es(case.A) + K * N * es(case.B) + M * N * es(case.C) * (2 if case.beta != 0 else 1)
+    if case.bias is not None:
+        b += N * es(case.bias)
     if case.fp8:
         b += 4 * (M * math.ceil(K / 128) + math.ceil(K / 128) * math.ceil(N / 128))
     return b, 2.0 * M * N * K
@@ -71,7 +76,7 @@ def algorithmic(case):
 
 def storage_bytes(case):
     tot = 0
-    for t in (case.A, case.B, case.C, case.A_scale, case.B_scale):
+    for t in (case.A, case.B, case.C, case.A_scale, case.B_scale, case.bias):
         if t is not None:
             tot += t.untyped_storage().nbytes()
     return tot
@@ -99,7 +104,7 @@ def rotated_sets(case, device, min_bytes=CACHE_DEFEAT_BYTES, max_sets=4096):
     for _ in range(P - 1):
         sets.append(synth.Case(d0.name, clone_view(d0.A), clone_view(d0.B), clone_view(d0.C),
                                d0.alpha, d0.beta, clone_view(d0.A_scale), clone_view(d0.B_scale),
-                               d0.rtol))
+                               d0.rtol, {}, clone_view(d0.bias), d0.act))
     return sets
 
 
@@ -112,9 +117,15 @@ class Call:
         import ctypes
         self.views = [dg.view_of(t) for t in ((c.A, c.A_scale, c.B, c.B_scale, c.C) if c.fp8
                                               else (c.A, c.B, c.C))]
-        self.args = [ctypes.byref(v) for v in self.views] + [c.alpha, c.beta, stream]
-        self.fn = dg.lib().dg_gemm_fp8 if c.fp8 else dg.lib().dg_gemm
+        self.args = [ctypes.byref(v) for v in self.views]
         self.name = "dg_gemm_fp8" if c.fp8 else "dg_gemm"
+        if c.fused:   # the fused-epilogue entry point: + bias view and activation code
+            self.bias = dg.view_of(c.bias) if c.bias is not None else None
+            act = {"none": dg.DG_ACT_NONE, "relu": dg.DG_ACT_RELU, "gelu_tanh": dg.DG_ACT_GELU_TANH}[c.act]
+            self.args += [ctypes.byref(self.bias) if self.bias is not None else None, act]
+            self.name += "_epilogue"
+        self.args += [c.alpha, c.beta, stream]
+        self.fn = getattr(dg.lib(), self.name)
 
     def __call__(self):
         return self.fn(*self.args)
@@ -233,13 +244,16 @@ def time_config(dg, name, reps=None, trials=5):
            "buffer_sets": len(sets), "tflops": round(tflops, 2),
            "frac_mfma_peak": round(tflops / MFMA_PEAK[dt], 4), "gbs": round(gbs, 1),
            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "dtype": dt, "mnk": list(case.mnk),
-           "path": re.search(r"path=(\S+)", plan).group(1)}
+           "c_elem_bytes": case.C.element_size(), "path": re.search(r"path=(\S+)", plan).group(1)}
     m = re.search(r"tile=(\S+)", plan)
     if m:
         rec["tile"] = m.group(1)
     m = re.search(r"splits=(\d+)", plan)
     if m:
         rec["splits"] = int(m.group(1))
+    if case.fused:
+        rec["epilogue"] = f"+bias({str(case.bias.dtype).split('.')[-1]}) {case.act}" if case.bias is not None \
+            else case.act
     del sets
     torch.cuda.empty_cache()
     return rec
@@ -324,7 +338,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--configs", default="all",
                     help="other workloads to time: all, none, or a comma list of "
-                         "c1,c3,c4,c5_128,c5_4096 (GEMMs) and q_a,q_b (the FP8 quantizer)")
+                         "c1,c3,c4,c5_128,c5_4096 (GEMMs), <config>_gelu (the same GEMM with a "
+                         "fused bias + GELU epilogue) and q_a,q_b (the FP8 quantizer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -405,10 +420,23 @@ def main():
     # ---- the other workloads
     others = {}
     names = [] if args.configs == "none" else (
-        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b"] if args.configs == "all" else args.configs.split(","))
+        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu"]
+        if args.configs == "all" else args.configs.split(","))
     for n in names:
         others[n] = time_quant(dg, n) if n in QUANT_CONFIGS else time_config(dg, n)
         log(n, json.dumps(others[n]))
+    # fused epilogue: its cost over the plain GEMM of the same operands, and the
+    # least a separate bias + GELU pass would add (read C and write it again
+    # once, at the HBM peak)
+    # (the plain x.W1 time is the step's second timed region)
+    plain_us = {n: r["us"] for n, r in others.items()}
+    plain_us["c2a"] = round(k_avg * 1e3, 3)
+    for n, r in others.items():
+        base = n[:-5] if n.endswith("_gelu") else None
+        if base in plain_us:
+            M, N = r["mnk"][0], r["mnk"][1]
+            r["vs_plain_us"] = round(r["us"] - plain_us[base], 3)
+            r["unfused_floor_us"] = round(plain_us[base] + 2 * M * N * r["c_elem_bytes"] / (HBM_PEAK_GBS * 1e3), 3)
 
     if args.copy_calib:
         copy_calibration()

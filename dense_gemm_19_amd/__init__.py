@@ -6,6 +6,7 @@ HIP kernels.  PyTorch provides the device memory and the current stream.
     import dense_gemm_19_amd as dg
     dg.gemm(A, B, C, alpha=1.0, beta=0.0)                     # C <- alpha*A@B + beta*C
     dg.gemm_fp8(qA, sA, qB, sB, C, alpha=1.0, beta=0.0)       # block-scaled E4M3
+    dg.gemm_epilogue(A, B, C, bias, dg.DG_ACT_GELU_TANH)       # C <- gelu(A@B + bias)
     print(dg.plan(A, B, C))                                    # the chosen plan, no launch
 
 Tensors may have any strides (transposes, padded rows, up to 4-D views whose
@@ -25,6 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libdg.so")
 
 # dg_dtype codes
 DG_F32, DG_F16, DG_BF16, DG_F8E4M3 = 0, 1, 2, 3
+# dg_act codes (fused epilogue activation)
+DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU_TANH = 0, 1, 2
 _DTYPE = {torch.float32: DG_F32, torch.float16: DG_F16, torch.bfloat16: DG_BF16,
           torch.float8_e4m3fn: DG_F8E4M3}
 
@@ -65,7 +68,12 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_size_t]
         L.dg_gemm_fp8_plan.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_char_p, ctypes.c_size_t]
-        for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan"):
+        L.dg_gemm_epilogue.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_void_p]
+        L.dg_gemm_fp8_epilogue.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_void_p]
+        for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan", "dg_gemm_epilogue",
+                  "dg_gemm_fp8_epilogue"):
             getattr(L, f).restype = ctypes.c_int
         L.dg_quant_fp8.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p]
         L.dg_quant_fp8.restype = ctypes.c_int
@@ -134,6 +142,30 @@ def gemm_fp8(A: torch.Tensor, A_scale: torch.Tensor, B: torch.Tensor, B_scale: t
     vs = [view_of(t) for t in (A, A_scale, B, B_scale, C)]
     _check(lib().dg_gemm_fp8(*[ctypes.byref(v) for v in vs], alpha, beta, _stream(stream)),
            "dg_gemm_fp8")
+    return C
+
+
+def gemm_epilogue(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: torch.Tensor | None = None,
+                  act: int = DG_ACT_NONE, alpha: float = 1.0, beta: float = 0.0,
+                  stream=None) -> torch.Tensor:
+    """C <- act(alpha * A @ B + beta * C + bias[None, :]) in one kernel; returns C."""
+    va, vb, vc = view_of(A), view_of(B), view_of(C)
+    vbias = view_of(bias) if bias is not None else None
+    _check(lib().dg_gemm_epilogue(ctypes.byref(va), ctypes.byref(vb), ctypes.byref(vc),
+                                  ctypes.byref(vbias) if vbias is not None else None, int(act),
+                                  alpha, beta, _stream(stream)), "dg_gemm_epilogue")
+    return C
+
+
+def gemm_fp8_epilogue(A: torch.Tensor, A_scale: torch.Tensor, B: torch.Tensor, B_scale: torch.Tensor,
+                      C: torch.Tensor, bias: torch.Tensor | None = None, act: int = DG_ACT_NONE,
+                      alpha: float = 1.0, beta: float = 0.0, stream=None) -> torch.Tensor:
+    """gemm_fp8 followed in the same kernel by + bias and the activation; returns C."""
+    vs = [view_of(t) for t in (A, A_scale, B, B_scale, C)]
+    vbias = view_of(bias) if bias is not None else None
+    _check(lib().dg_gemm_fp8_epilogue(*[ctypes.byref(v) for v in vs],
+                                      ctypes.byref(vbias) if vbias is not None else None, int(act),
+                                      alpha, beta, _stream(stream)), "dg_gemm_fp8_epilogue")
     return C
 
 

@@ -1,5 +1,5 @@
 // device_common.hpp -- gfx950 device helpers: vector types, output conversion,
-// the alpha/beta epilogue store.
+// the epilogue store (alpha/beta, bias, activation).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -70,13 +70,40 @@ __device__ __forceinline__ float sum_partials(int S, Load load) {
     return s;
 }
 
-// out = alpha * acc + beta * C_in (C_in read only when beta != 0), rounded to the
-// C dtype and stored at (m, n).  The caller has checked m < M and n < N.
+// GELU in its tanh form (Hendrycks and Gimpel, "Gaussian Error Linear Units",
+// 2016): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).  Evaluated as
+// x * sigmoid(2u), u = sqrt(2/pi) (x + 0.044715 x^3), which is the same
+// function (0.5 (1 + tanh u) = 1 / (1 + e^(-2u))) without the cancellation of
+// 1 + tanh(u) for negative x.  exp2 and the reciprocal are gfx950's own
+// instructions (about 1 ulp each); e^(-2u) = 2^(-2u log2 e).  Large negative x
+// gives e = +inf and a zero of x's sign; large positive x gives x.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// act(v): Act numbering.  ReLU keeps NaN (v < 0 is false for NaN) and -0.
+__device__ __forceinline__ float activate(int act, float v) {
+    if (act == ACT_RELU) return v < 0.0f ? 0.0f : v;
+    if (act == ACT_GELU_TANH) return gelu_tanh(v);
+    return v;
+}
+
+// bias[n] as FP32 (exact for every bias dtype).  The caller has checked e.bias.
+__device__ __forceinline__ float load_bias(const Epilogue &e, int64_t n) {
+    return load_out(e.bias + n * e.bias_s, e.bias_kind);
+}
+
+// out = act(alpha * acc + beta * C_in + bias[n]) (C_in read only when beta != 0,
+// bias only when given), rounded to the C dtype and stored at (m, n).  The
+// caller has checked m < M and n < N.
 __device__ __forceinline__ void epilogue_store(const Epilogue &e, int64_t m, int64_t n, float acc) {
     char *p = e.C + m * e.c_rs + n * e.c_cs;
     float v = e.alpha * acc;
     if (e.beta != 0.0f) v = fmaf(e.beta, load_out(p, e.out_kind), v);
-    store_out(p, e.out_kind, v);
+    if (e.bias) v += load_bias(e, n);
+    store_out(p, e.out_kind, activate(e.act, v));
 }
 
 }  // namespace dg

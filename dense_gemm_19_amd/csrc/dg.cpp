@@ -30,7 +30,8 @@ bool env_on(const char *name) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 dg_status validate(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
-                   const dg_view *C, float alpha, float beta, bool fp8, Problem *out) {
+                   const dg_view *C, const dg_view *bias, int act, float alpha, float beta, bool fp8,
+                   Problem *out) {
     Problem p;
     p.fp8 = fp8;
     dg_status st;
@@ -70,6 +71,16 @@ dg_status validate(const dg_view *A, const dg_view *SA, const dg_view *B, const 
     // kernels index M, N and K with 32-bit integers
     if (p.M > INT32_MAX || p.N > INT32_MAX || p.K > INT32_MAX) return DG_ERR_OVERFLOW;
 
+    // fused epilogue: the bias is one row of N values of a C-capable dtype
+    if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU_TANH) return DG_ERR_INVALID_ARG;
+    p.act = act;
+    if (bias) {
+        if ((st = canonicalize(bias, &p.bias)) != DG_SUCCESS) return st;
+        if (p.bias.dtype != DG_F32 && p.bias.dtype != DG_F16 && p.bias.dtype != DG_BF16) return DG_ERR_DTYPE;
+        if (p.bias.rows != 1 || p.bias.cols != p.N) return DG_ERR_SHAPE_MISMATCH;
+        p.has_bias = true;
+    }
+
     if (!std::isfinite(alpha) || !std::isfinite(beta)) return DG_ERR_NONFINITE_SCALAR;
     p.alpha = alpha;
     p.beta = beta;
@@ -78,6 +89,7 @@ dg_status validate(const dg_view *A, const dg_view *SA, const dg_view *B, const 
     if (self_overlaps(p.C)) return DG_ERR_STRIDE;
     if (spans_overlap(p.C, p.A) || spans_overlap(p.C, p.B)) return DG_ERR_ALIAS;
     if (fp8 && (spans_overlap(p.C, p.SA) || spans_overlap(p.C, p.SB))) return DG_ERR_ALIAS;
+    if (p.has_bias && spans_overlap(p.C, p.bias)) return DG_ERR_ALIAS;
     *out = p;
     return DG_SUCCESS;
 }
@@ -204,6 +216,10 @@ Epilogue make_epi(const Problem &p) {
     e.out_kind = p.out_kind;
     e.alpha = p.alpha;
     e.beta = p.beta;
+    e.bias = p.has_bias && !p.bias.empty() ? p.bias.ptr : nullptr;
+    e.bias_s = p.bias.cs;
+    e.bias_kind = p.bias.dtype;   // dg_dtype and OutKind agree for F32 / F16 / BF16
+    e.act = p.act;
     return e;
 }
 
@@ -274,15 +290,17 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
 }
 
 dg_status entry(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
-                const dg_view *C, float alpha, float beta, bool fp8, hipStream_t stream) {
+                const dg_view *C, const dg_view *bias, int act, float alpha, float beta, bool fp8,
+                hipStream_t stream) {
     Problem p;
-    dg_status st = validate(A, SA, B, SB, C, alpha, beta, fp8, &p);
+    dg_status st = validate(A, SA, B, SB, C, bias, act, alpha, beta, fp8, &p);
     if (st != DG_SUCCESS) return st;
     Device d;
     if ((st = current_device(&d, true)) != DG_SUCCESS) return st;
     if (!d.gfx950) return DG_ERR_ARCH;
     if (env_on("DG_CHECK_POINTERS")) {
-        const Mat *ms[] = {&p.A, &p.B, &p.C, fp8 ? &p.SA : nullptr, fp8 ? &p.SB : nullptr};
+        const Mat *ms[] = {&p.A, &p.B, &p.C, fp8 ? &p.SA : nullptr, fp8 ? &p.SB : nullptr,
+                           p.has_bias ? &p.bias : nullptr};
         for (const Mat *m : ms)
             if (m && !m->empty() && (st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
     }
@@ -293,7 +311,7 @@ dg_status plan_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
                      const dg_view *C, float alpha, float beta, bool fp8, char *buf, size_t len) {
     if (!buf && len) return DG_ERR_INVALID_ARG;
     Problem p;
-    dg_status st = validate(A, SA, B, SB, C, alpha, beta, fp8, &p);
+    dg_status st = validate(A, SA, B, SB, C, nullptr, DG_ACT_NONE, alpha, beta, fp8, &p);
     if (st != DG_SUCCESS) return st;
     Device d;
     int count = 0;
@@ -366,13 +384,24 @@ dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_
 
 dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,
                   hipStream_t stream) {
-    return dg::entry(A, nullptr, B, nullptr, C, alpha, beta, false, stream);
+    return dg::entry(A, nullptr, B, nullptr, C, nullptr, DG_ACT_NONE, alpha, beta, false, stream);
+}
+
+dg_status dg_gemm_epilogue(const dg_view *A, const dg_view *B, const dg_view *C, const dg_view *bias,
+                           dg_act act, float alpha, float beta, hipStream_t stream) {
+    return dg::entry(A, nullptr, B, nullptr, C, bias, (int)act, alpha, beta, false, stream);
 }
 
 dg_status dg_gemm_fp8(const dg_view *A, const dg_view *A_scale, const dg_view *B,
                       const dg_view *B_scale, const dg_view *C, float alpha, float beta,
                       hipStream_t stream) {
-    return dg::entry(A, A_scale, B, B_scale, C, alpha, beta, true, stream);
+    return dg::entry(A, A_scale, B, B_scale, C, nullptr, DG_ACT_NONE, alpha, beta, true, stream);
+}
+
+dg_status dg_gemm_fp8_epilogue(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                               const dg_view *B_scale, const dg_view *C, const dg_view *bias, dg_act act,
+                               float alpha, float beta, hipStream_t stream) {
+    return dg::entry(A, A_scale, B, B_scale, C, bias, (int)act, alpha, beta, true, stream);
 }
 
 dg_status dg_gemm_plan(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,

@@ -3,10 +3,10 @@
 // Split-K (sheratonhq.com deep dive, section 5.2): partial sums of S slices of K
 // arrive in an FP32 workspace [S][M][N]; this kernel adds them in the fixed
 // order s = 0..S-1, so a plan always produces the same bits, then applies
-// out = alpha * sum + beta * C_in and rounds to the C dtype.
-// When alpha == 0 (or K == 0) the product is never formed: C <- beta * C, and
-// with beta == 0 as well C <- 0 without reading it (kwkr.cn article, section
-// 4.3, records a kernel that skipped the beta scaling when alpha was 0).
+// out = act(alpha * sum + beta * C_in + bias) and rounds to the C dtype.
+// When alpha == 0 (or K == 0) the product is never formed: C <- act(beta * C +
+// bias), and with beta == 0 C is not read (kwkr.cn article, section 4.3,
+// records a kernel that skipped the beta scaling when alpha was 0).
 #include "device_common.hpp"
 
 namespace dg {
@@ -29,8 +29,9 @@ __global__ void __launch_bounds__(NT) scale_c(ScaleArgs p) {
     for (int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * NT) {
         const int64_t m = idx / p.N, n = idx - m * p.N;
         char *q = p.epi.C + m * p.epi.c_rs + n * p.epi.c_cs;
-        const float v = (p.epi.beta != 0.0f) ? p.epi.beta * load_out(q, p.epi.out_kind) : 0.0f;
-        store_out(q, p.epi.out_kind, v);
+        float v = (p.epi.beta != 0.0f) ? p.epi.beta * load_out(q, p.epi.out_kind) : 0.0f;
+        if (p.epi.bias) v += load_bias(p.epi, n);
+        store_out(q, p.epi.out_kind, activate(p.epi.act, v));
     }
 }
 

@@ -420,14 +420,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     // ---- epilogue: element (i, j, e) of a wave is C[mb + 16i + e][nb + 16j]
     const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
     const Epilogue &ep = p.epi;
-    auto store = [&](auto OUTK, int m, int n, float a) __attribute__((always_inline)) {
+    // FUSED: bias (read once per column) and activation after alpha/beta.
+    auto store = [&](auto OUTK, auto FUSED, int m, int n, float a, float bias) __attribute__((always_inline)) {
         constexpr int ok = decltype(OUTK)::value;
         char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
         float v = ep.alpha * a;
         if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, ok), v);
+        if constexpr (decltype(FUSED)::value) {
+            if (ep.bias) v += bias;
+            v = activate(ep.act, v);
+        }
         store_out(q, ok, v);
     };
-    auto finish = [&](auto OUTK) __attribute__((always_inline)) {
+    auto finish = [&](auto OUTK, auto FUSED) __attribute__((always_inline)) {
+        float bias[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bias[j] = decltype(FUSED)::value && ep.bias && nb + 16 * j < p.N ? load_bias(ep, nb + 16 * j) : 0.0f;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -436,14 +445,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = mb + 16 * i + e;
-                    if (m < p.M && n < p.N) store(OUTK, m, n, acc[i][j][e]);
+                    if (m < p.M && n < p.N) store(OUTK, FUSED, m, n, acc[i][j][e], bias[j]);
                 }
             }
     };
+    auto finish_kind = [&](auto FUSED) __attribute__((always_inline)) {
+        if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{}, FUSED);
+        else if (ep.out_kind == OUT_BF16) finish(std::integral_constant<int, OUT_BF16>{}, FUSED);
+        else finish(std::integral_constant<int, OUT_F16>{}, FUSED);
+    };
     auto finish_any = [&]() __attribute__((always_inline)) {
-        if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{});
-        else if (ep.out_kind == OUT_BF16) finish(std::integral_constant<int, OUT_BF16>{});
-        else finish(std::integral_constant<int, OUT_F16>{});
+        if (ep.plain()) finish_kind(std::false_type{});
+        else finish_kind(std::true_type{});
     };
     // Split K is a separate instantiation (SPLIT), so that the kernels without
     // it keep their registers; it exists for tiles of at most 64 accumulator

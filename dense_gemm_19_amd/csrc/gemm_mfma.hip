@@ -217,13 +217,18 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
 // ------------------------------------------------------------------ epilogue
 
 // Store a wave's accumulators: element (i, j, e) is C[mb + 16i + e][nb + 16j].
-// OUTK < 0: FP32 split-K partial into ws[z]; otherwise alpha/beta epilogue and
-// conversion to the C dtype.  One instantiation per output kind keeps the fully
-// unrolled body small enough for the accumulators to stay in registers.
-template <int TM, int TN, int OUTK>
+// OUTK < 0: FP32 split-K partial into ws[z]; otherwise the epilogue and
+// conversion to the C dtype (FUSED: with the bias, read once per column, and
+// the activation).  One instantiation per output kind keeps the fully unrolled
+// body small enough for the accumulators to stay in registers.
+template <int TM, int TN, int OUTK, bool FUSED>
 __device__ __forceinline__ void write_tile(const f32x4 (&acc)[TM][TN], const MfmaArgs &p, int mb, int nb,
                                            int z) {
     const Epilogue &ep = p.epi;
+    float bias[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+        bias[j] = FUSED && ep.bias && nb + 16 * j < p.N ? load_bias(ep, nb + 16 * j) : 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -240,6 +245,10 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[TM][TN], const Mfm
                         char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
                         float v = ep.alpha * a;
                         if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, OUTK), v);
+                        if (FUSED) {
+                            if (ep.bias) v += bias[j];
+                            v = activate(ep.act, v);
+                        }
                         store_out(q, OUTK, v);
                     }
                 }
@@ -366,10 +375,14 @@ __global__ void __launch_bounds__(NT) mfma_gemm(MfmaArgs p) {
 
     // Epilogue: lane holds D rows 4*(lane/16) + e, column lane%16 of each block.
     const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
-    if (p.splits > 1) write_tile<TM, TN, -1>(acc, p, mb, nb, z);
-    else if (p.epi.out_kind == OUT_F32) write_tile<TM, TN, OUT_F32>(acc, p, mb, nb, z);
-    else if (p.epi.out_kind == OUT_BF16) write_tile<TM, TN, OUT_BF16>(acc, p, mb, nb, z);
-    else write_tile<TM, TN, OUT_F16>(acc, p, mb, nb, z);
+    if (p.splits > 1) write_tile<TM, TN, -1, false>(acc, p, mb, nb, z);
+    else if (!p.epi.plain()) {
+        if (p.epi.out_kind == OUT_F32) write_tile<TM, TN, OUT_F32, true>(acc, p, mb, nb, z);
+        else if (p.epi.out_kind == OUT_BF16) write_tile<TM, TN, OUT_BF16, true>(acc, p, mb, nb, z);
+        else write_tile<TM, TN, OUT_F16, true>(acc, p, mb, nb, z);
+    } else if (p.epi.out_kind == OUT_F32) write_tile<TM, TN, OUT_F32, false>(acc, p, mb, nb, z);
+    else if (p.epi.out_kind == OUT_BF16) write_tile<TM, TN, OUT_BF16, false>(acc, p, mb, nb, z);
+    else write_tile<TM, TN, OUT_F16, false>(acc, p, mb, nb, z);
 }
 
 template <int IN, int BM, int BN, int AM, int BMd, int SLOW>

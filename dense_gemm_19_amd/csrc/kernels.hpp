@@ -29,11 +29,20 @@ struct Operand {
     int vec;            // 1: 16-byte vector loads are legal for full chunks
 };
 
+// Element-wise activation applied after the bias (numbering matches dg_act).
+enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
+
+// out[m][n] = act(alpha * acc + beta * C_in[m][n] + bias[n]), rounded to the C dtype.
 struct Epilogue {
     char *C;
     int64_t c_rs, c_cs; // bytes
     int out_kind;       // OutKind
     float alpha, beta;  // beta == 0: C is not read
+    const char *bias;   // N-vector added to every row, or null (no bias)
+    int64_t bias_s;     // bytes between consecutive bias elements (0: one value for every column)
+    int bias_kind;      // OutKind numbering: OUT_F32 / OUT_F16 / OUT_BF16
+    int act;            // Act
+    constexpr bool plain() const { return bias == nullptr && act == ACT_NONE; }
 };
 
 struct MfmaArgs {
@@ -84,7 +93,7 @@ struct ReduceArgs {
     int M, N, S;
 };
 
-struct ScaleArgs {      // C <- beta * C (beta == 0: C <- 0), for alpha == 0 or K == 0
+struct ScaleArgs {      // C <- act(beta * C + bias) (beta == 0: C not read), for alpha == 0 or K == 0
     Epilogue epi;
     int M, N;
 };

@@ -33,6 +33,10 @@ struct Problem {
     Mat A, B, C, SA, SB;
     int64_t M = 0, N = 0, K = 0;
     float alpha = 1.f, beta = 0.f;
+    // fused epilogue (no influence on the plan): bias N-vector and activation
+    bool has_bias = false;
+    Mat bias;
+    int act = ACT_NONE;
 };
 
 enum class Path : int { Noop = 0, Scale = 1, Skinny = 2, Mfma = 3 };

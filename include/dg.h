@@ -15,6 +15,8 @@
  *    article, sections 2.1 and 3.2 (strides are bytes, not elements).
  *  - FP8 with scale factors applied in the kernel: sheratonhq.com deep dive,
  *    section 2.4.
+ *  - Bias + activation fused into the GEMM's epilogue: "DeepGEMM is not a new
+ *    model" article (cf-1.com), section 3.3.
  *
  * Conventions shared by every entry point
  *  - Views are borrowed for the duration of the call only; the caller owns all
@@ -115,6 +117,46 @@ dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C,
 dg_status dg_gemm_fp8(const dg_view *A, const dg_view *A_scale, const dg_view *B,
                       const dg_view *B_scale, const dg_view *C, float alpha, float beta,
                       hipStream_t stream);
+
+/* Activation of the fused epilogue (dg_gemm_epilogue, dg_gemm_fp8_epilogue). */
+typedef enum {
+    DG_ACT_NONE = 0,
+    DG_ACT_RELU = 1,       /* x < 0 ? 0 : x (NaN stays NaN) */
+    DG_ACT_GELU_TANH = 2   /* GELU, tanh form (Hendrycks and Gimpel, 2016):
+                              0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+} dg_act;
+
+/*
+ * GEMM with a fused epilogue: the bias add and the activation run on the
+ * accumulators in registers, and C is written once ("DeepGEMM is not a new
+ * model" article, cf-1.com, section 3.3: GEMM + BiasAdd + GeLU in one kernel
+ * instead of three global-memory round trips):
+ *
+ *   C[m,n] <- act(alpha * (A*B)[m,n] + beta * C[m,n] + bias[n])
+ *
+ * (A*B)[m,n] is the FP32-accumulated product of dg_gemm (FP16/BF16 A and B),
+ * or of dg_gemm_fp8 with its scales (the _fp8 form).  The sum is formed in
+ * FP32 in that order (alpha * AB, then + beta * C with one rounding, then
+ * + bias), the activation is evaluated in FP32 and the result rounded once to
+ * C's dtype.
+ *   bias: NULL (no bias), or a view of N elements (shape [N] or [1, N]) of
+ *         dtype DG_F32, DG_F16 or DG_BF16 with any element stride >= 0
+ *         (0: one value for every column).  Read only; it must not overlap C.
+ *   act:  a dg_act value.
+ * alpha == 0 or K == 0: C <- act(beta * C + bias).  With bias == NULL and
+ * act == DG_ACT_NONE the result is bit for bit that of dg_gemm / dg_gemm_fp8.
+ * Every other argument, rule and error as for dg_gemm / dg_gemm_fp8, plus:
+ * DG_ERR_INVALID_ARG (act not a dg_act value), DG_ERR_DTYPE (bias dtype),
+ * DG_ERR_SHAPE_MISMATCH (bias not 1 x N), DG_ERR_ALIAS (bias overlaps C), and
+ * the view errors of the bias view itself.
+ */
+dg_status dg_gemm_epilogue(const dg_view *A, const dg_view *B, const dg_view *C,
+                           const dg_view *bias, dg_act act, float alpha, float beta,
+                           hipStream_t stream);
+
+dg_status dg_gemm_fp8_epilogue(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                               const dg_view *B_scale, const dg_view *C, const dg_view *bias,
+                               dg_act act, float alpha, float beta, hipStream_t stream);
 
 /*
  * Validate the arguments of dg_gemm exactly as dg_gemm does and write a

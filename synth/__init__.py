@@ -19,6 +19,8 @@ Recipe (every draw is seeded and reproducible):
       c5_128 / c5_4096  FP8 E4M3, M in {128, 4096}, N=7168, K=4096, sources
            N(0,1), quantized per (row, 128-wide K block) for A and per 128x128
            block for B, BF16 C
+      <config>_gelu  the same operands with a fused epilogue: BF16 bias
+           N(0,1) of N elements drawn from rng(201), then GELU (tanh form)
   * The FP8 quantizer stands in for the producer of quantized activations and
     weights: s = max(amax, 1e-12) / 448 in FP32, q = clamp(x / s, -448, 448)
     cast to float8_e4m3fn with torch (RNE).  The GEMM consumes (q, s) as given,
@@ -115,6 +117,8 @@ class Case:
     B_scale: torch.Tensor | None = None
     rtol: float = 1e-4
     extra: dict = field(default_factory=dict)
+    bias: torch.Tensor | None = None   # fused epilogue: N-vector added to every row
+    act: str = "none"                  # fused epilogue: "none", "relu" or "gelu_tanh"
 
     @property
     def fp8(self) -> bool:
@@ -135,7 +139,12 @@ class Case:
             dev_st = torch.empty(st.nbytes(), dtype=torch.uint8).set_(st).to(device).untyped_storage()
             return base.set_(dev_st, t.storage_offset(), t.shape, t.stride())
         return Case(self.name, mv(self.A), mv(self.B), mv(self.C), self.alpha, self.beta,
-                    mv(self.A_scale), mv(self.B_scale), self.rtol, dict(self.extra))
+                    mv(self.A_scale), mv(self.B_scale), self.rtol, dict(self.extra), mv(self.bias),
+                    self.act)
+
+    @property
+    def fused(self) -> bool:
+        return self.bias is not None or self.act != "none"
 
 
 def gemm_case(M, N, K, in_dtype=torch.bfloat16, out_dtype=torch.float32, seed=0,
@@ -182,6 +191,33 @@ def fp8_case(M, N, K, seed=0, out_dtype=torch.bfloat16, alpha=1.0, beta=0.0, dis
     return Case(name or f"fp8_{M}x{N}x{K}", qa, qb, c, alpha, beta, sa, sb, rtol=1e-3)
 
 
+def bias_vector(N: int, dtype=torch.bfloat16, seed=0, layout="contig", scale=1.0) -> torch.Tensor:
+    """The epilogue's bias: N(0, scale^2) draws from its own generator rng(seed).
+    layout "contig": N adjacent elements; "strided": every other element of a
+    2N buffer (the gaps hold NaN); "bcast": one drawn value seen through
+    stride 0."""
+    g = rng(seed)
+    if layout == "bcast":
+        return to_dtype(draw(g, (1,), "normal", scale), dtype).expand(N)
+    v = to_dtype(draw(g, (N,), "normal", scale), dtype)
+    if layout == "contig":
+        return v
+    if layout == "strided":
+        st = torch.full((2 * max(N, 1),), float("nan"), dtype=dtype)
+        st[0:2 * N:2] = v
+        return st[0:2 * N:2]
+    raise ValueError(layout)
+
+
+def with_epilogue(case: Case, act: str, bias_dtype=torch.bfloat16, bias_layout="contig",
+                  seed=0, bias_scale=1.0, name=None) -> Case:
+    """The same operands with a fused bias (bias_dtype None: no bias) and activation."""
+    N = case.mnk[1]
+    bias = None if bias_dtype is None else bias_vector(N, bias_dtype, seed, bias_layout, bias_scale)
+    return Case(name or f"{case.name}+{act}", case.A, case.B, case.C, case.alpha, case.beta,
+                case.A_scale, case.B_scale, case.rtol, dict(case.extra), bias, act)
+
+
 def c4_strided_a(g: np.random.Generator, dtype=torch.bfloat16) -> torch.Tensor:
     """A as a (1,64,64,4096) view of a (1,64,64,4160) tensor whose row pitch is
     padded by 64 elements; the pad holds NaN so a stray read shows up."""
@@ -213,6 +249,10 @@ def config(name: str) -> Case:
         return fp8_case(128, 7168, 4096, seed=106, name="c5_128")
     if name == "c5_4096":
         return fp8_case(4096, 7168, 4096, seed=107, name="c5_4096")
+    if name.endswith("_gelu") and name[:-5] in CONFIGS:
+        # the same operands, then a BF16 bias N(0,1) from rng(seed 201) and GELU
+        return with_epilogue(config(name[:-5]), "gelu_tanh", torch.bfloat16, "contig", seed=201,
+                             name=name)
     raise KeyError(name)
 
 

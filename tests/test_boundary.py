@@ -26,6 +26,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan", "dg_status_str",
+            "dg_gemm_epilogue", "dg_gemm_fp8_epilogue",
             "dg_version", "dg_calib_mfma", "dg_calib_read", "dg_calib_launch"} <= set(names)
     L = dg.lib()
     for n in names:
@@ -240,3 +241,42 @@ def test_quant_validation():
     assert q(X, mat(BASE + 0x1000000, M, K, 0, 1, DG_F8E4M3), S_tok, 0) == "DG_ERR_STRIDE"   # Q rows collide
     Xe = mat(BASE, 0, K, 2 * K, 2, DG_BF16)
     assert q(Xe, mat(BASE + 0x1000000, 0, K, K, 1, DG_F8E4M3), mat(BASE + 0x2000000, 0, 3, 12, 4, DG_F32), 0) == "DG_SUCCESS"
+
+
+def test_epilogue_validation():
+    """dg_gemm_epilogue / dg_gemm_fp8_epilogue reject a bad bias or activation
+    before touching a device (include/dg.h); a valid call gets past validation
+    (on a machine without a GPU it then stops at the device query)."""
+    import ctypes
+    L = dg.lib()
+    A, B, C = ok_triplet(64, 96, 64)
+    bias = lambda ptr, n, es, dt: make_view(ptr, (n,), (es,), dt)
+    good = bias(BASE + 0x30000000, 96, 2, DG_BF16)
+    e = lambda bb, act: dg.STATUS[L.dg_gemm_epilogue(ctypes.byref(A), ctypes.byref(B), ctypes.byref(C),
+                                                     ctypes.byref(bb) if bb is not None else None, act,
+                                                     1.0, 0.0, None)]
+    assert e(good, 3) == "DG_ERR_INVALID_ARG"
+    assert e(good, -1) == "DG_ERR_INVALID_ARG"
+    assert e(bias(BASE + 0x30000000, 96, 1, DG_F8E4M3), 2) == "DG_ERR_DTYPE"
+    assert e(bias(BASE + 0x30000000, 95, 2, DG_BF16), 2) == "DG_ERR_SHAPE_MISMATCH"
+    assert e(make_view(BASE + 0x30000000, (96, 1), (2, 2), DG_BF16), 2) == "DG_ERR_SHAPE_MISMATCH"   # a column
+    assert e(bias(BASE + 0x20000000 + 4 * 96 * 10, 96, 4, DG_F32), 2) == "DG_ERR_ALIAS"   # a row of C
+    assert e(bias(BASE + 0x30000001, 96, 2, DG_BF16), 2) == "DG_ERR_MISALIGNED"
+    assert e(bias(0, 96, 2, DG_BF16), 2) == "DG_ERR_NULL"
+    for bb in (good, bias(BASE + 0x30000000, 96, 0, DG_F32), make_view(BASE + 0x30000000, (1, 96), (192, 2), DG_F16),
+               None):
+        for act in (0, 1, 2):
+            assert e(bb, act) in ("DG_ERR_HIP", "DG_ERR_ARCH", "DG_SUCCESS"), (bb, act)
+    # FP8 form: the same checks after the scale views
+    M, N, K = 64, 256, 256
+    qa = mat(BASE, M, K, K, 1, DG_F8E4M3)
+    sa = mat(BASE + 0x1000000, M, 2, 8, 4, DG_F32)
+    qb = mat(BASE + 0x2000000, K, N, N, 1, DG_F8E4M3)
+    sb = mat(BASE + 0x3000000, 2, 2, 8, 4, DG_F32)
+    c = mat(BASE + 0x4000000, M, N, 2 * N, 2, DG_BF16)
+    f = lambda bb, act: dg.STATUS[L.dg_gemm_fp8_epilogue(*[ctypes.byref(v) for v in (qa, sa, qb, sb, c)],
+                                                         ctypes.byref(bb), act, 1.0, 0.0, None)]
+    assert f(bias(BASE + 0x5000000, N, 2, DG_BF16), 7) == "DG_ERR_INVALID_ARG"
+    assert f(bias(BASE + 0x5000000, N - 1, 2, DG_BF16), 2) == "DG_ERR_SHAPE_MISMATCH"
+    assert f(bias(BASE + 0x4000000, N, 2, DG_BF16), 2) == "DG_ERR_ALIAS"
+    assert f(bias(BASE + 0x5000000, N, 2, DG_BF16), 2) in ("DG_ERR_HIP", "DG_ERR_ARCH", "DG_SUCCESS")
