@@ -31,7 +31,9 @@ The JSON line also carries:
                 token, q_b: B per 128x128 block; GB/s against HBM peak), and
                 the fused bias + GELU epilogue on three of the GEMMs (*_gelu:
                 vs_plain_us is its cost over the plain GEMM, unfused_floor_us
-                the least a separate bias + GELU pass over C would take).
+                the least a separate bias + GELU pass over C would take), and
+                moe8: the 8 MoE expert GEMMs [1,512] x [512,4096] in one
+                dg_gemm_grouped call, against the same GEMMs as 8 dg_gemm calls.
 """
 from __future__ import annotations
 
@@ -199,6 +201,72 @@ def time_quant(dg, name, trials=5):
             "path": "quant", "algorithmic_bytes": nbytes}
 
 
+def time_grouped(dg, trials=5):
+    """The MoE experts (8 x [1,512] x [512,4096], one token row shared): one
+    dg_gemm_grouped call per step against the same 8 GEMMs as 8 dg_gemm calls,
+    both over rotated buffer sets."""
+    import ctypes
+    import torch
+    import synth
+    experts = synth.moe_experts()
+    E = len(experts)
+    d0 = [c.to("cuda:0") for c in experts]
+    x = d0[0].A
+    per = sum(storage_bytes(c) for c in d0) - (E - 1) * x.untyped_storage().nbytes()
+    P = max(2, -(-CACHE_DEFEAT_BYTES // per))
+    sets = [d0] + [[synth.Case(c.name, x, clone_view(c.B), clone_view(c.C)) for c in d0] for _ in range(P - 1)]
+    stream = torch.cuda.current_stream().cuda_stream
+    L = dg.lib()
+
+    class Grouped:
+        name = "dg_gemm_grouped"
+
+        def __init__(self, cs):
+            self.a = dg._view_array([c.A for c in cs])
+            self.b = dg._view_array([c.B for c in cs])
+            self.c = dg._view_array([c.C for c in cs])
+
+        def __call__(self):
+            return L.dg_gemm_grouped(E, self.a, self.b, self.c, 1.0, 0.0, stream)
+
+    grouped = [Grouped(cs) for cs in sets]
+    separate = [Call(dg, c, stream) for cs in sets for c in cs]
+    nbytes = sum(algorithmic(c)[0] for c in experts) - (E - 1) * algorithmic_a_bytes(experts[0])
+
+    def timed(calls, per_step):
+        reps = 200
+        run_checked(calls, range(10 * per_step))
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(trials):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run_checked(calls, range(reps * per_step))
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        ts.sort()
+        return ts[len(ts) // 2], ts[0]
+
+    tg, tg_min = timed(grouped, 1)
+    ts_, ts_min = timed(separate, E)
+    plan = dg.grouped_plan([c.A for c in d0], [c.B for c in d0], [c.C for c in d0])
+    del sets, grouped, separate, d0
+    torch.cuda.empty_cache()
+    return {"us": round(tg * 1e6, 3), "us_min": round(tg_min * 1e6, 3), "buffer_sets": P,
+            "gbs": round(nbytes / tg / 1e9, 1), "frac_hbm_peak": round(nbytes / tg / 1e9 / HBM_PEAK_GBS, 4),
+            "separate_us": round(ts_ * 1e6, 3), "separate_gbs": round(nbytes / ts_ / 1e9, 1),
+            "speedup_vs_separate": round(ts_ / tg, 3), "dtype": "bf16", "mnk": [1, 4096, 512],
+            "experts": E, "path": "skinny grouped", "plan": plan, "algorithmic_bytes": nbytes}
+
+
+def algorithmic_a_bytes(case):
+    """Bytes of the A operand (read once however many groups share it)."""
+    M, N, K = case.mnk
+    return M * K * case.A.element_size()
+
+
 def run_checked(calls, idx):
     """Launch calls[i % len] for i in idx; raise on the first non-zero status."""
     n = len(calls)
@@ -339,7 +407,8 @@ def main():
     ap.add_argument("--configs", default="all",
                     help="other workloads to time: all, none, or a comma list of "
                          "c1,c3,c4,c5_128,c5_4096 (GEMMs), <config>_gelu (the same GEMM with a "
-                         "fused bias + GELU epilogue) and q_a,q_b (the FP8 quantizer)")
+                         "fused bias + GELU epilogue), q_a,q_b (the FP8 quantizer) and moe8 (8 MoE "
+                         "expert GEMMs in one grouped call)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -420,10 +489,11 @@ def main():
     # ---- the other workloads
     others = {}
     names = [] if args.configs == "none" else (
-        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu"]
+        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu", "moe8"]
         if args.configs == "all" else args.configs.split(","))
     for n in names:
-        others[n] = time_quant(dg, n) if n in QUANT_CONFIGS else time_config(dg, n)
+        others[n] = (time_quant(dg, n) if n in QUANT_CONFIGS else time_grouped(dg) if n == "moe8"
+                     else time_config(dg, n))
         log(n, json.dumps(others[n]))
     # fused epilogue: its cost over the plain GEMM of the same operands, and the
     # least a separate bias + GELU pass would add (read C and write it again
@@ -472,6 +542,8 @@ def main():
     if measured:
         out["roofline"]["frac_of_measured"] = round(achieved / measured["hbm_read_gbs"], 4)
         for n, r in others.items():
+            if "gbs" not in r:
+                continue
             if "tflops" in r:
                 peak = measured["mfma_fp8_tflops"] if r["dtype"] == "fp8" else measured["mfma_bf16_tflops"]
                 r["frac_measured_mfma"] = round(r["tflops"] / peak, 4)

@@ -72,8 +72,11 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_void_p]
         L.dg_gemm_fp8_epilogue.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_grouped.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_grouped_plan.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_char_p, ctypes.c_size_t]
         for f in ("dg_gemm", "dg_gemm_fp8", "dg_gemm_plan", "dg_gemm_fp8_plan", "dg_gemm_epilogue",
-                  "dg_gemm_fp8_epilogue"):
+                  "dg_gemm_fp8_epilogue", "dg_gemm_grouped", "dg_gemm_grouped_plan"):
             getattr(L, f).restype = ctypes.c_int
         L.dg_quant_fp8.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p]
         L.dg_quant_fp8.restype = ctypes.c_int
@@ -167,6 +170,37 @@ def gemm_fp8_epilogue(A: torch.Tensor, A_scale: torch.Tensor, B: torch.Tensor, B
                                       ctypes.byref(vbias) if vbias is not None else None, int(act),
                                       alpha, beta, _stream(stream)), "dg_gemm_fp8_epilogue")
     return C
+
+
+def _view_array(ts):
+    arr = (View * max(len(ts), 1))()
+    for i, t in enumerate(ts):
+        arr[i] = view_of(t)
+    return arr
+
+
+def gemm_grouped(As, Bs, Cs, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C[g] <- alpha * A[g] @ B[g] + beta * C[g] for every g, in as few launches as
+    the shapes allow (lists of tensors of equal length); returns Cs."""
+    if not (len(As) == len(Bs) == len(Cs)):
+        raise ValueError("A, B and C lists differ in length")
+    a, b, c = _view_array(As), _view_array(Bs), _view_array(Cs)
+    _check(lib().dg_gemm_grouped(len(As), a, b, c, alpha, beta, _stream(stream)), "dg_gemm_grouped")
+    return Cs
+
+
+def grouped_plan_views(G: int, a, b, c, alpha: float = 1.0, beta: float = 0.0):
+    """(status, description) of dg_gemm_grouped_plan for view arrays a, b, c."""
+    buf = ctypes.create_string_buffer(4096)
+    st = lib().dg_gemm_grouped_plan(G, a, b, c, alpha, beta, buf, len(buf))
+    return st, buf.value.decode()
+
+
+def grouped_plan(As, Bs, Cs, alpha: float = 1.0, beta: float = 0.0) -> str:
+    """Describe the launches dg_gemm_grouped would make for these tensors."""
+    st, text = grouped_plan_views(len(As), _view_array(As), _view_array(Bs), _view_array(Cs), alpha, beta)
+    _check(st, "dg_gemm_grouped_plan")
+    return text
 
 
 def plan_views(A: View, B: View, C: View, alpha: float = 1.0, beta: float = 0.0,

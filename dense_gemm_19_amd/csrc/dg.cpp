@@ -12,6 +12,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "dg.h"
 #include "kernels.hpp"
@@ -330,6 +332,190 @@ dg_status plan_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
     return DG_SUCCESS;
 }
 
+// Grouped GEMM (dg_gemm_grouped) ---------------------------------------------
+//
+// Every group is validated as dg_gemm validates it; groups run concurrently, so
+// no group's C may overlap another group's A, B or C (inputs may be shared).
+// The groups whose plan is the N-contiguous streaming kernel (M <= 8, the
+// decode-time experts of an MoE layer) are launched together, one grid per M
+// class (1, 2, 4, 8) and per SKINNY_GROUP_MAX groups; each such group's K split
+// is planned for its share of the CUs (its column slabs over the batch's), so
+// the whole grid fills the device about once.  Every other group runs through
+// its own plan, in order, on the same stream.
+
+struct GroupBatch {
+    int mclass = 1;
+    std::vector<int> groups;
+    std::vector<Plan> plans;
+    int units = 0, lds = 0;
+    size_t ws_floats = 0, counters = 0;
+};
+
+struct GroupedPlan {
+    std::vector<GroupBatch> batches;
+    std::vector<int> solo;           // groups launched one by one (empty ones excluded)
+};
+
+int64_t slabs_of(const Problem &p) { return cdiv(p.N, SKINNY_BN_COLS); }
+
+GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
+    GroupedPlan gp;
+    std::vector<int> cls[4];
+    for (int g = 0; g < (int)ps.size(); ++g) {
+        const Plan pl = cached_plan(ps[g], d);
+        if (pl.path == Path::Noop) continue;
+        if (pl.path == Path::Skinny && pl.sk_kind == SK_BN) {
+            const int c = pl.sk_mmax == 1 ? 0 : pl.sk_mmax == 2 ? 1 : pl.sk_mmax == 4 ? 2 : 3;
+            cls[c].push_back(g);
+        } else {
+            gp.solo.push_back(g);
+        }
+    }
+    for (int c = 0; c < 4; ++c) {
+        for (size_t i0 = 0; i0 < cls[c].size(); i0 += SKINNY_GROUP_MAX) {
+            GroupBatch b;
+            b.mclass = 1 << c;
+            const size_t i1 = std::min(cls[c].size(), i0 + SKINNY_GROUP_MAX);
+            int64_t total = 0;
+            for (size_t i = i0; i < i1; ++i) total += slabs_of(ps[cls[c][i]]);
+            for (size_t i = i0; i < i1; ++i) {
+                const int g = cls[c][i];
+                Device share = d;   // this group's share of the CUs
+                share.cus = (int)std::max<int64_t>(1, (int64_t)d.cus * slabs_of(ps[g]) / total);
+                const Plan pl = cached_plan(ps[g], share);
+                b.groups.push_back(g);
+                b.plans.push_back(pl);
+                b.units += (int)(slabs_of(ps[g]) * pl.splits);
+                b.lds = std::max(b.lds, skinny_bn_lds(b.mclass, pl.sk_kc));
+                if (pl.splits > 1) {
+                    b.ws_floats += (size_t)pl.splits * (size_t)ps[g].M * (size_t)ps[g].N;
+                    b.counters += (size_t)slabs_of(ps[g]);
+                }
+            }
+            gp.batches.push_back(std::move(b));
+        }
+    }
+    return gp;
+}
+
+dg_status validate_grouped(int G, const dg_view *A, const dg_view *B, const dg_view *C, float alpha,
+                           float beta, std::vector<Problem> *out) {
+    if (G < 0) return DG_ERR_INVALID_ARG;
+    if (G > 0 && (!A || !B || !C)) return DG_ERR_NULL;
+    std::vector<Problem> ps((size_t)G);
+    dg_status st;
+    for (int g = 0; g < G; ++g)
+        if ((st = validate(&A[g], nullptr, &B[g], nullptr, &C[g], nullptr, DG_ACT_NONE, alpha, beta, false,
+                           &ps[g])) != DG_SUCCESS)
+            return st;
+    for (int g = 1; g < G; ++g)
+        if (ps[g].in_kind != ps[0].in_kind) return DG_ERR_DTYPE;
+    for (int g = 0; g < G; ++g) {
+        if (ps[g].C.empty()) continue;
+        for (int h = 0; h < G; ++h) {
+            if (h == g) continue;
+            if (spans_overlap(ps[g].C, ps[h].A) || spans_overlap(ps[g].C, ps[h].B) ||
+                spans_overlap(ps[g].C, ps[h].C))
+                return DG_ERR_ALIAS;
+        }
+    }
+    *out = std::move(ps);
+    return DG_SUCCESS;
+}
+
+dg_status grouped_entry(int G, const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,
+                        hipStream_t stream) {
+    std::vector<Problem> ps;
+    dg_status st = validate_grouped(G, A, B, C, alpha, beta, &ps);
+    if (st != DG_SUCCESS || G == 0) return st;
+    Device d;
+    if ((st = current_device(&d, true)) != DG_SUCCESS) return st;
+    if (!d.gfx950) return DG_ERR_ARCH;
+    if (env_on("DG_CHECK_POINTERS")) {
+        for (const Problem &p : ps)
+            for (const Mat *m : {&p.A, &p.B, &p.C})
+                if (!m->empty() && (st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
+    }
+    const GroupedPlan gp = plan_grouped(ps, d);
+    for (const GroupBatch &b : gp.batches) {
+        float *ws = nullptr;
+        int *counters = nullptr;
+        if (b.ws_floats > 0 &&
+            get_workspace(stream, b.ws_floats * sizeof(float), b.counters, &ws, &counters) != hipSuccess) {
+            (void)hipGetLastError();
+            return DG_ERR_HIP;
+        }
+        GroupedSkinnyArgs ga;
+        std::memset(&ga, 0, sizeof ga);
+        ga.ngroups = (int)b.groups.size();
+        size_t wofs = 0, cofs = 0;
+        int unit = 0;
+        for (size_t i = 0; i < b.groups.size(); ++i) {
+            const Problem &p = ps[b.groups[i]];
+            const Plan &pl = b.plans[i];
+            SkinnyArgs &a = ga.g[i];
+            a.A = p.A.ptr; a.a_rs = p.A.rs; a.a_cs = p.A.cs;
+            a.B = p.B.ptr; a.b_rs = p.B.rs; a.b_cs = p.B.cs;
+            a.epi = make_epi(p);
+            a.ws = pl.splits > 1 ? ws + wofs : nullptr;
+            a.counters = pl.splits > 1 ? counters + cofs : nullptr;
+            a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+            a.in_kind = p.in_kind;
+            a.a_vec = pl.sk_a_vec;
+            a.splits = pl.splits;
+            a.k_per_split = pl.sk_k_per_split;
+            a.kc = pl.sk_kc;
+            if (pl.splits > 1) {
+                wofs += (size_t)pl.splits * (size_t)p.M * (size_t)p.N;
+                cofs += (size_t)slabs_of(p);
+            }
+            ga.unit_begin[i] = unit;
+            ga.slabs[i] = (int)slabs_of(p);
+            unit += ga.slabs[i] * pl.splits;
+        }
+        ga.unit_begin[ga.ngroups] = unit;
+        if (launch_skinny_grouped(ps[0].in_kind, b.mclass, ga, b.units, b.lds, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return DG_ERR_HIP;
+        }
+    }
+    for (int g : gp.solo)
+        if ((st = run(ps[g], d, stream)) != DG_SUCCESS) return st;
+    if (env_on("DG_SYNC_DEBUG")) {
+        if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return DG_ERR_HIP;
+    }
+    return DG_SUCCESS;
+}
+
+dg_status grouped_plan_entry(int G, const dg_view *A, const dg_view *B, const dg_view *C, float alpha,
+                             float beta, char *buf, size_t len) {
+    if (!buf && len) return DG_ERR_INVALID_ARG;
+    std::vector<Problem> ps;
+    dg_status st = validate_grouped(G, A, B, C, alpha, beta, &ps);
+    if (st != DG_SUCCESS) return st;
+    Device d;
+    int count = 0;
+    if (hipGetDeviceCount(&count) == hipSuccess && count > 0) {
+        if ((st = current_device(&d, false)) != DG_SUCCESS) return st;
+    } else {
+        (void)hipGetLastError();
+        d = Device();
+    }
+    const GroupedPlan gp = plan_grouped(ps, d);
+    std::string out = "G=" + std::to_string(G);
+    for (const GroupBatch &b : gp.batches) {
+        out += " | batch mmax=" + std::to_string(b.mclass) + " units=" + std::to_string(b.units) +
+               " lds=" + std::to_string(b.lds) + " groups=";
+        for (size_t i = 0; i < b.groups.size(); ++i)
+            out += (i ? "," : "") + std::to_string(b.groups[i]) + ":s" + std::to_string(b.plans[i].splits);
+    }
+    out += " | solo=";
+    for (size_t i = 0; i < gp.solo.size(); ++i) out += (i ? "," : "") + std::to_string(gp.solo[i]);
+    if (len) std::snprintf(buf, len, "%s", out.c_str());
+    if (d.present && !d.gfx950) return DG_ERR_ARCH;
+    return DG_SUCCESS;
+}
+
 // FP8 quantizer (dg_quant_fp8): validate X, Q, S as include/dg.h states, then
 // launch one 256-thread workgroup per 128 x 128 tile of X.
 dg_status quant_entry(const dg_view *X, const dg_view *Q, const dg_view *S, int mode, hipStream_t stream) {
@@ -380,6 +566,16 @@ extern "C" {
 dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_quant_mode mode,
                        hipStream_t stream) {
     return dg::quant_entry(X, Q, S, (int)mode, stream);
+}
+
+dg_status dg_gemm_grouped(int32_t G, const dg_view *A, const dg_view *B, const dg_view *C, float alpha,
+                          float beta, hipStream_t stream) {
+    return dg::grouped_entry(G, A, B, C, alpha, beta, stream);
+}
+
+dg_status dg_gemm_grouped_plan(int32_t G, const dg_view *A, const dg_view *B, const dg_view *C, float alpha,
+                               float beta, char *buf, size_t len) {
+    return dg::grouped_plan_entry(G, A, B, C, alpha, beta, buf, len);
 }
 
 dg_status dg_gemm(const dg_view *A, const dg_view *B, const dg_view *C, float alpha, float beta,

@@ -87,6 +87,20 @@ inline int skinny_bn_lds(int mmax, int kc) {
     return a > r ? a : r;
 }
 
+// Grouped SK_BN launch (several independent thin GEMMs in one grid): workgroup
+// u belongs to the group g with unit_begin[g] <= u < unit_begin[g + 1] and runs
+// that group's column slab (u - unit_begin[g]) % slabs[g] and K split
+// (u - unit_begin[g]) / slabs[g].  Passed by value (kernel arguments are at
+// most 4 KB), so one launch holds at most SKINNY_GROUP_MAX groups.
+constexpr int SKINNY_GROUP_MAX = 16;
+struct GroupedSkinnyArgs {
+    int ngroups;
+    int unit_begin[SKINNY_GROUP_MAX + 1];
+    int slabs[SKINNY_GROUP_MAX];
+    SkinnyArgs g[SKINNY_GROUP_MAX];
+};
+static_assert(sizeof(GroupedSkinnyArgs) <= 4096, "kernel arguments are limited to 4 KB");
+
 struct ReduceArgs {
     const float *ws;    // [S][M][N]
     Epilogue epi;
@@ -122,6 +136,10 @@ hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const 
                            hipStream_t stream);
 hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
                          hipStream_t stream);
+// m_max: the largest M class of the groups (1, 2, 4 or 8); lds_bytes: the
+// largest skinny_bn_lds of the groups.
+hipError_t launch_skinny_grouped(int in_kind, int m_max, const GroupedSkinnyArgs &args, int units,
+                                 int lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);
 

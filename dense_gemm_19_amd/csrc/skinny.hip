@@ -22,6 +22,10 @@
 //   order.  K is split so that the grid holds at most one workgroup per CU;
 //   the last workgroup of a slab to finish (an arrival counter) adds the S
 //   partials in the order s = 0..S-1, so the sum does not depend on timing.
+// skinny_bn_grouped runs several SK_BN problems in one grid: the experts of an
+//   MoE layer, each a small GEMM such as [1,512] x [512,4096] (cf-1.com
+//   article, section 1), whose separate launches would each pay the launch
+//   cost (section 5.1 of that article) and leave most CUs idle.
 // SK_BK: B is K-contiguous (B = K_cache^T: column n is row n of the cache).  A
 //   wave owns one column; lanes take 8 consecutive K values each per 512-wide K
 //   step, with up to 8 steps' loads of B and A issued before any is used, then a
@@ -71,8 +75,9 @@ constexpr int BN_U = 8;                         // consecutive rows per lane per
 constexpr int BN_SWEEP = BN_WAVES * BN_R * BN_U;
 static_assert(BN_COLS == BN_W * 8 && BN_SWEEP == SKINNY_BN_SWEEP, "shared with the planner");
 
+// One workgroup's share of an SK_BN problem: column slab `slab`, K split `z`.
 template <int MMAX, int IN>
-__global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
+__device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int slab, const int z) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // LDS: A chunk as 16-bit values [MMAX][kc] (kc a multiple of BN_SWEEP), later
     // reused for the cross-wave reduction red[wave][m][BN_COLS].
@@ -81,12 +86,11 @@ __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
     __shared__ int is_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % BN_W, r = lane / BN_W;
-    const int n0 = blockIdx.x * BN_COLS + c * 8;
-    const int z = blockIdx.y;
+    const int n0 = slab * BN_COLS + c * 8;
     const int kb = z * p.k_per_split;
     const int ke = min(kb + p.k_per_split, p.K);
     // every column of the slab exists: the vector path (uniform over the workgroup)
-    const bool slab_full = (blockIdx.x + 1) * BN_COLS <= p.N;
+    const bool slab_full = (slab + 1) * BN_COLS <= p.N;
     const char *bcol = p.B + (int64_t)n0 * p.b_cs;
 
     float acc[MMAX][8];
@@ -237,7 +241,7 @@ __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
     __syncthreads();
     for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
         const int m = t / BN_COLS, col = t - m * BN_COLS;
-        const int n = blockIdx.x * BN_COLS + col;
+        const int n = slab * BN_COLS + col;
         if (m < p.M && n < p.N) {
             float s = red[m * BN_COLS + col];
 #pragma unroll
@@ -261,14 +265,14 @@ __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-        is_last = __hip_atomic_fetch_add(p.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+        is_last = __hip_atomic_fetch_add(p.counters + slab, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
     __syncthreads();
     if (!is_last) return;
     const int64_t plane = (int64_t)p.M * p.N;
     for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
         const int m = t / BN_COLS, col = t - m * BN_COLS;
-        const int n = blockIdx.x * BN_COLS + col;
+        const int n = slab * BN_COLS + col;
         if (m < p.M && n < p.N) {
             float *w = p.ws + (int64_t)m * p.N + n;
             const float s = sum_partials(p.splits, [&](int q) {
@@ -277,7 +281,24 @@ __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
             epilogue_store(p.epi, m, n, s);
         }
     }
-    if (tid == 0) __hip_atomic_store(p.counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(p.counters + slab, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MMAX, int IN>
+__global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
+    skinny_bn_body<MMAX, IN>(p, blockIdx.x, blockIdx.y);
+}
+
+// Several SK_BN problems in one grid (the experts of an MoE layer, say): the
+// group of this workgroup is found by a scan of at most SKINNY_GROUP_MAX
+// uniform values, then the workgroup runs exactly what skinny_bn would.
+template <int MMAX, int IN>
+__global__ void __launch_bounds__(BN_NT) skinny_bn_grouped(GroupedSkinnyArgs p) {
+    const int u = blockIdx.x;
+    int g = 0;
+    while (g + 1 < p.ngroups && u >= p.unit_begin[g + 1]) ++g;
+    const int local = u - p.unit_begin[g];
+    skinny_bn_body<MMAX, IN>(p.g[g], local % p.slabs[g], local / p.slabs[g]);
 }
 
 // ------------------------------------------------------------------ SK_BK
@@ -390,12 +411,44 @@ hipError_t launch_m(int kind, int m_max, const SkinnyArgs &a, int grid_x, int wa
     return hipErrorInvalidValue;
 }
 
+template <int MMAX, int IN>
+hipError_t launch_grouped_k(const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
+    if (lds > 48 * 1024) {
+        static int attr = 0;   // benign race: setting the attribute twice is harmless
+        if (lds > attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn_grouped<MMAX, IN>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+            attr = lds;
+        }
+    }
+    hipLaunchKernelGGL((skinny_bn_grouped<MMAX, IN>), dim3(units), dim3(BN_NT), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int IN>
+hipError_t launch_grouped_m(int m_max, const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
+    switch (m_max) {
+    case 1: return launch_grouped_k<1, IN>(a, units, lds, s);
+    case 2: return launch_grouped_k<2, IN>(a, units, lds, s);
+    case 4: return launch_grouped_k<4, IN>(a, units, lds, s);
+    case 8: return launch_grouped_k<8, IN>(a, units, lds, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
                          hipStream_t stream) {
     if (args.in_kind == IN_BF16) return launch_m<IN_BF16>(kind, m_max, args, grid_x, waves, stream);
     return launch_m<IN_F16>(kind, m_max, args, grid_x, waves, stream);
+}
+
+hipError_t launch_skinny_grouped(int in_kind, int m_max, const GroupedSkinnyArgs &args, int units,
+                                 int lds_bytes, hipStream_t stream) {
+    if (in_kind == IN_BF16) return launch_grouped_m<IN_BF16>(m_max, args, units, lds_bytes, stream);
+    return launch_grouped_m<IN_F16>(m_max, args, units, lds_bytes, stream);
 }
 
 }  // namespace dg

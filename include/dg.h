@@ -159,6 +159,42 @@ dg_status dg_gemm_fp8_epilogue(const dg_view *A, const dg_view *A_scale, const d
                                dg_act act, float alpha, float beta, hipStream_t stream);
 
 /*
+ * Grouped GEMM: G independent problems in one call,
+ *
+ *   C[g] <- alpha * A[g] * B[g] + beta * C[g],   g = 0 .. G-1,
+ *
+ * e.g. the experts of an MoE layer applied to the tokens routed to each: the
+ * "DeepGEMM is not a new model" article (cf-1.com), section 1, singles out the
+ * small per-expert GEMM [1,512] x [512,4096] issued once per expert, whose cost
+ * is dominated by launching it (about 1.2 us per launch, its section 5.1).
+ *   A, B, C: host arrays of G views each (read during the call only).  Every
+ *         group obeys every rule of dg_gemm; groups may differ in M, N, K,
+ *         strides and C dtype, but A and B have one dtype (DG_F16 or DG_BF16)
+ *         across all groups.  Input views may be shared between groups (one
+ *         token row sent to several experts); no group's C may overlap any
+ *         group's A, B or C.
+ *   G == 0: nothing happens.
+ * Execution: groups with M <= 8 whose B is N-contiguous with 16-byte aligned
+ * rows run together in one launch per M class (1, 2, 4, 8) and per 16 groups;
+ * every other group runs through its own dg_gemm plan, in order, on `stream`.
+ * Results equal those of G separate dg_gemm calls within the dg_gemm tolerance
+ * (a group's K may be split differently), and are bitwise reproducible.
+ * Errors: DG_ERR_INVALID_ARG (G < 0), DG_ERR_NULL (an array is NULL with
+ * G > 0), the dg_gemm error of the first invalid group, DG_ERR_DTYPE (A/B
+ * dtypes differ between groups), DG_ERR_ALIAS (a C overlaps another group's
+ * operand).  Validation errors enqueue nothing; a launch failure (DG_ERR_HIP)
+ * may leave earlier launches of the call enqueued.
+ */
+dg_status dg_gemm_grouped(int32_t G, const dg_view *A, const dg_view *B, const dg_view *C,
+                          float alpha, float beta, hipStream_t stream);
+
+/* Validate as dg_gemm_grouped does and describe its launches (batches of
+ * grouped groups with their K splits, and the groups run alone) in buf,
+ * without launching anything.  buf may be NULL only if len == 0. */
+dg_status dg_gemm_grouped_plan(int32_t G, const dg_view *A, const dg_view *B, const dg_view *C,
+                               float alpha, float beta, char *buf, size_t len);
+
+/*
  * Validate the arguments of dg_gemm exactly as dg_gemm does and write a
  * one-line, NUL-terminated description of the chosen plan (path, tiles,
  * split-K, grid, canonical operand layouts) into buf[0..len-1], without

@@ -19,6 +19,8 @@ Recipe (every draw is seeded and reproducible):
       c5_128 / c5_4096  FP8 E4M3, M in {128, 4096}, N=7168, K=4096, sources
            N(0,1), quantized per (row, 128-wide K block) for A and per 128x128
            block for B, BF16 C
+      moe8 8 MoE experts, x[1,512] . W_e[512,4096] (cf-1.com article, section 1),
+           BF16, x shared (one token routed to all 8), N(0,1), seed 108
       <config>_gelu  the same operands with a fused epilogue: BF16 bias
            N(0,1) of N elements drawn from rng(201), then GELU (tanh form)
   * The FP8 quantizer stands in for the producer of quantized activations and
@@ -216,6 +218,23 @@ def with_epilogue(case: Case, act: str, bias_dtype=torch.bfloat16, bias_layout="
     bias = None if bias_dtype is None else bias_vector(N, bias_dtype, seed, bias_layout, bias_scale)
     return Case(name or f"{case.name}+{act}", case.A, case.B, case.C, case.alpha, case.beta,
                 case.A_scale, case.B_scale, case.rtol, dict(case.extra), bias, act)
+
+
+def moe_experts(E=8, M=1, K=512, N=4096, seed=108, dtype=torch.bfloat16, out_dtype=torch.bfloat16,
+                shared_x=True) -> list:
+    """E expert GEMMs x . W_e (the token rows routed to each expert times that
+    expert's [K, N] row-major weight): x N(0,1) [M, K] (one tensor shared by all
+    experts when shared_x, else one per expert, drawn first), then W_0 .. W_{E-1}
+    N(0,1); C write-only (NaN-filled)."""
+    g = rng(seed)
+    xs = [to_dtype(draw(g, (M, K), "normal"), dtype)] if shared_x else \
+        [to_dtype(draw(g, (M, K), "normal"), dtype) for _ in range(E)]
+    cases = []
+    for e in range(E):
+        W = to_dtype(draw(g, (K, N), "normal"), dtype)
+        C = torch.full((M, N), float("nan"), dtype=out_dtype)
+        cases.append(Case(f"expert{e}", xs[0] if shared_x else xs[e], W, C))
+    return cases
 
 
 def c4_strided_a(g: np.random.Generator, dtype=torch.bfloat16) -> torch.Tensor:

@@ -280,3 +280,50 @@ def test_epilogue_validation():
     assert f(bias(BASE + 0x5000000, N - 1, 2, DG_BF16), 2) == "DG_ERR_SHAPE_MISMATCH"
     assert f(bias(BASE + 0x4000000, N, 2, DG_BF16), 2) == "DG_ERR_ALIAS"
     assert f(bias(BASE + 0x5000000, N, 2, DG_BF16), 2) in ("DG_ERR_HIP", "DG_ERR_ARCH", "DG_SUCCESS")
+
+
+def test_grouped_validation_and_plan():
+    """dg_gemm_grouped_plan validates every group and batches the thin
+    N-contiguous groups (include/dg.h)."""
+    import ctypes
+    V = dg.View
+    def arr(vs):
+        a = (V * max(len(vs), 1))()
+        for i, v in enumerate(vs):
+            a[i] = v
+        return a
+    def gp(As, Bs, Cs, alpha=1.0, beta=0.0):
+        st, text = dg.grouped_plan_views(len(As), arr(As), arr(Bs), arr(Cs), alpha, beta)
+        return dg.STATUS[st], text
+    E = 8
+    x = mat(BASE, 1, 512, 1024, 2)
+    Ws = [mat(BASE + (1 + e) * 0x1000000, 512, 4096, 8192, 2) for e in range(E)]
+    Cs = [mat(BASE + (20 + e) * 0x1000000, 1, 4096, 8192, 2) for e in range(E)]
+    st, text = gp([x] * E, Ws, Cs)
+    assert st == "DG_SUCCESS", text
+    assert "batch mmax=1 units=256" in text and "solo= " not in text and text.endswith("solo="), text
+    # 40 groups: three batches of at most 16
+    st, text = gp([x] * 40, [Ws[0]] * 40, [mat(BASE + (40 + e) * 0x1000000, 1, 4096, 8192, 2) for e in range(40)])
+    assert st == "DG_SUCCESS" and text.count("batch mmax=1") == 3, text
+    # a group with M = 20 runs alone; a K-contiguous B runs alone
+    A20 = mat(BASE, 20, 512, 1024, 2)
+    Bk = mat(BASE + 0x3000000, 512, 128, 2, 1024)
+    st, text = gp([x, A20, x], [Ws[0], Ws[1], Bk], [Cs[0], mat(BASE + 0x30000000, 20, 4096, 8192, 2),
+                                                    mat(BASE + 0x31000000, 1, 128, 256, 2)])
+    assert st == "DG_SUCCESS" and text.endswith("solo=1,2"), text
+    assert gp([], [], [])[0] == "DG_SUCCESS"
+    L = dg.lib()
+    assert dg.STATUS[L.dg_gemm_grouped_plan(-1, None, None, None, 1.0, 0.0, None, 0)] == "DG_ERR_INVALID_ARG"
+    assert dg.STATUS[L.dg_gemm_grouped_plan(2, None, None, None, 1.0, 0.0, None, 0)] == "DG_ERR_NULL"
+    assert dg.STATUS[L.dg_gemm_grouped(-1, None, None, None, 1.0, 0.0, None)] == "DG_ERR_INVALID_ARG"
+    # two groups writing one C, or one C inside another group's input
+    assert gp([x, x], Ws[:2], [Cs[0], Cs[0]])[0] == "DG_ERR_ALIAS"
+    x_in_c0 = mat(BASE + (20 + 0) * 0x1000000, 1, 512, 1024, 2)   # group 1 reads what group 0 writes
+    assert gp([x, x_in_c0], Ws[:2], Cs[:2])[0] == "DG_ERR_ALIAS"
+    assert gp([x, x], [Ws[0], Ws[1]], [Cs[0], mat(BASE + 0x1000000 + 64, 1, 4096, 8192, 2)])[0] == "DG_ERR_ALIAS"
+    # dtype mix across groups; a bad group reports its own error
+    x16 = mat(BASE, 1, 512, 1024, 2, DG_F16)
+    W16 = mat(BASE + 0x1000000, 512, 4096, 8192, 2, DG_F16)
+    assert gp([x, x16], [Ws[0], W16], Cs[:2])[0] == "DG_ERR_DTYPE"
+    assert gp([x, x], [Ws[0], mat(BASE + 0x2000000, 511, 4096, 8192, 2)], Cs[:2])[0] == "DG_ERR_SHAPE_MISMATCH"
+    assert gp([x, x], Ws[:2], Cs[:2], alpha=float("nan"))[0] == "DG_ERR_NONFINITE_SCALAR"
