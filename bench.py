@@ -26,7 +26,8 @@ The JSON line also carries:
                 frac_measured_* divide by these instead of the data-sheet peaks;
   configs       every other workload shape timed the same way (TFLOPS and the
                 fraction of the dense MFMA peak for M >= 64, GB/s and the
-                fraction of HBM peak for the thin and HBM-bound shapes), the
+                fraction of HBM peak for the thin and HBM-bound shapes; c5_tail is
+                an FP8 shape whose last wave of tiles is short), the
                 FP8 quantizer producing the FP8 GEMM's operands (q_a: A per
                 token, q_b: B per 128x128 block; GB/s against HBM peak), and
                 the fused bias + GELU epilogue on three of the GEMMs (*_gelu:
@@ -406,7 +407,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--configs", default="all",
                     help="other workloads to time: all, none, or a comma list of "
-                         "c1,c3,c4,c5_128,c5_4096 (GEMMs), <config>_gelu (the same GEMM with a "
+                         "c1,c3,c4,c5_128,c5_4096,c5_tail (GEMMs), <config>_gelu (the same GEMM with a "
                          "fused bias + GELU epilogue), q_a,q_b (the FP8 quantizer) and moe8 (8 MoE "
                          "expert GEMMs in one grouped call)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -489,7 +490,8 @@ def main():
     # ---- the other workloads
     others = {}
     names = [] if args.configs == "none" else (
-        ["c1", "c3", "c4", "c5_128", "c5_4096", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu", "moe8"]
+        ["c1", "c3", "c4", "c5_128", "c5_4096", "c5_tail", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu",
+         "moe8"]
         if args.configs == "all" else args.configs.split(","))
     for n in names:
         others[n] = (time_quant(dg, n) if n in QUANT_CONFIGS else time_grouped(dg) if n == "moe8"

@@ -271,6 +271,7 @@ dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
         a.kt_per_split = pl.kt_per_split;
         a.splits = pl.splits;
         a.group_m = pl.group_m;
+        a.dp_tiles = pl.dp_tiles;
         e = pl.dtl ? launch_mfma_dtl(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, a, stream)
                    : launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
     }

@@ -212,10 +212,15 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 // ------------------------------------------------------------------ tile raster (as gemm_mfma.hip)
 
-__device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int group_m,
-                                        int &tm, int &tn) {
-    int t = bid;
-    if ((nblk & 7) == 0) t = (bid & 7) * (nblk >> 3) + (bid >> 3);
+// Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b % 8); when
+// the count is a multiple of 8 this permutation hands each XCD a contiguous
+// run of work units, so neighbouring tiles share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+    return (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+}
+
+// Tile t of the raster: groups of group_m tile rows, walked column by column.
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
     const int per_group = group_m * tiles_n;
     const int grp = t / per_group;
     const int first_m = grp * group_m;
@@ -238,11 +243,16 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
 // instructions (every wave issues the same two, so all waves count the same
 // number of loads per tile).
 //
-// Split-K (grid.z = S > 1): each workgroup writes its FP32 partial tile with
-// agent-scope stores; the last of the S workgroups of a tile (arrival counter)
-// sums the partials in the order s = 0..S-1, applies the epilogue, and re-arms
-// the counter (sheratonhq.com deep dive, section 5.2, with a fixed summation
-// order so that the bits do not depend on which workgroup finishes last).
+// Split K (SPLIT, S = p.splits > 1): the first p.dp_tiles tiles run whole; each
+// later tile runs as S pieces of K.  A piece writes its FP32 partial tile with
+// agent-scope stores; the last of a tile's S pieces (arrival counter) sums the
+// partials in the order s = 0..S-1, applies the epilogue, and re-arms the
+// counter (sheratonhq.com deep dive, section 5.2, with a fixed summation order
+// so that the bits do not depend on which piece finishes last).  With
+// p.dp_tiles = 0 that is plain split K; with whole waves of tiles in front it
+// is a Stream-K-style hybrid: the pieces of the leftover tiles fill the last
+// wave of workgroup slots instead of leaving part of it idle (sheratonhq.com
+// deep dive, section 5.2, names Stream-K for balancing tails).
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
@@ -267,12 +277,22 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
+    // Work unit: units 0 .. dp_tiles-1 are whole tiles; later units are the S
+    // pieces z of the remaining tiles, a tile's pieces consecutive.
+    int t, z = 0, S = 1;
+    if (!SPLIT || (int)blockIdx.x < p.dp_tiles) {
+        t = xcd_remap(blockIdx.x, SPLIT ? p.dp_tiles : (int)gridDim.x);
+    } else {
+        const int pc = xcd_remap(blockIdx.x - p.dp_tiles, (int)gridDim.x - p.dp_tiles);
+        S = p.splits;
+        t = p.dp_tiles + pc / S;
+        z = pc - (pc / S) * S;
+    }
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int z = blockIdx.z;
-    const int kt0 = z * p.kt_per_split;
-    const int kt1 = min(kt0 + p.kt_per_split, p.ktiles);
+    const int kt0 = S == 1 ? 0 : z * p.kt_per_split;
+    const int kt1 = S == 1 ? p.ktiles : min(kt0 + p.kt_per_split, p.ktiles);
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -462,50 +482,53 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     // it keep their registers; it exists for tiles of at most 64 accumulator
     // registers per lane (the reduction stages partials beside them).
     static_assert(!SPLIT || TM * TN <= 16, "split K only for small tiles");
-    if (!SPLIT) {
+    if (!SPLIT || S == 1) {
         finish_any();
         return;
     }
-    // split K: publish this workgroup's partial tile (agent-scope stores are
-    // coherent across the XCDs' L2 caches), wait for the stores, take a ticket
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = nb + 16 * j;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = mb + 16 * i + e;
-                if (m < p.M && n < p.N)
-                    __hip_atomic_store(p.ws + ((int64_t)z * p.M + m) * p.N + n, acc[i][j][e], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int tile = tm * p.tiles_n + tn;
-    if (tid == 0)
-        is_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  p.splits - 1;
-    __syncthreads();
-    if (!is_last) return;
-    // The sum runs over s = 0..S-1 in order, this workgroup's own partial
-    // included; for each s all of the thread's elements are loaded together
-    // (one round trip per split, not one per split and element).
-    auto part = [&](int q, int m, int n) __attribute__((always_inline)) {
-        return __hip_atomic_load(p.ws + ((int64_t)q * p.M + min(m, p.M - 1)) * p.N + min(n, p.N - 1),
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // split K: publish this piece's partial tile (agent-scope stores are
+    // coherent across the XCDs' L2 caches), wait for the stores, take a ticket.
+    // Partials of split tile w = t - dp_tiles live at
+    //   ws[((w * S + q) * NW + wave) * (TM * TN * 4) + element) * 64 + lane]:
+    // every thread writes and reads its own elements (the last piece runs the
+    // same thread layout), each store or load instruction covers 256
+    // contiguous bytes, and rows or columns past the matrix need no test.
+    const int64_t piece = (int64_t)BM * BN;
+    const float *wtile = p.ws + (int64_t)(t - p.dp_tiles) * S * piece + (int64_t)wave * (TM * TN * 4 * 64) + lane;
+    auto slot = [&](int q, int i, int j, int e) __attribute__((always_inline)) {
+        return const_cast<float *>(wtile) + q * piece + ((i * TN + j) * 4 + e) * 64;
     };
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, mb + 16 * i + e, nb + 16 * j);
+            for (int e = 0; e < 4; ++e)
+                __hip_atomic_store(slot(z, i, j, e), acc[i][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int tile = tm * p.tiles_n + tn;
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  S - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // The sum runs over s = 0..S-1 in order, this workgroup's own partial
+    // included; for each s all of the thread's elements are loaded together
+    // (one round trip per split, not one per split and element).
+    auto part = [&](int q, int i, int j, int e) __attribute__((always_inline)) {
+        return __hip_atomic_load(slot(q, i, j, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, i, j, e);
     // (IB 16-row blocks of a split at a time: at most 8 fragments of partials
     // in registers beside the accumulators)
     constexpr int IB = TM < (8 / TN > 0 ? 8 / TN : 1) ? TM : (8 / TN > 0 ? 8 / TN : 1);
-    for (int q = 1; q < p.splits; ++q) {
+    for (int q = 1; q < S; ++q) {
 #pragma unroll
         for (int i0 = 0; i0 < TM; i0 += IB) {
             f32x4 v[IB][TN];
@@ -514,7 +537,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, mb + 16 * (i0 + i) + e, nb + 16 * j);
+                    for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, i0 + i, j, e);
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -528,8 +551,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd>
 hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
-    dim3 grid(a.tiles_m * a.tiles_n, 1, a.splits);
+    const int tiles = a.tiles_m * a.tiles_n;
+    dim3 grid(tiles);
     if (a.splits > 1) {
+        grid = dim3(a.dp_tiles + (tiles - a.dp_tiles) * a.splits);
         if constexpr (TM * TN <= 16) {
             hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true>), grid, dim3(64 * WGM * WGN), 0, s, a);
             return hipGetLastError();

@@ -55,10 +55,19 @@ struct MfmaArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int ktiles;                 // ceil(K / BK)
-    int kt_per_split;           // K tiles handled by one grid.z slice
+    int kt_per_split;           // K tiles handled by one split piece
     int splits;                 // S
     int group_m;                // tile raster: group of tile rows walked together
+    // Direct-to-LDS kernel with S > 1: the first dp_tiles tiles (in raster
+    // order) run whole, one workgroup each; every later tile runs as S pieces of
+    // kt_per_split K tiles, whose partials the tile's last piece adds up.  The
+    // grid is dp_tiles + (tiles - dp_tiles) * S workgroups (1-D).  dp_tiles = 0
+    // is plain split K; dp_tiles > 0 fills the last, partial wave of workgroups
+    // with pieces of the tiles left over by the whole waves (a Stream-K-style
+    // hybrid).  The register-staged kernel ignores it (grid.z = S).
+    int dp_tiles;
 };
+
 
 struct SkinnyArgs {
     const char *A; int64_t a_rs, a_cs;   // M x K
@@ -117,6 +126,10 @@ struct ScaleArgs {      // C <- act(beta * C + bias) (beta == 0: C not read), fo
 enum MfmaTile : int { T256x256 = 0, T128x128 = 1, T64x64 = 2, T128x64 = 3, T64x128 = 4, NUM_MFMA_TILES = 5 };
 inline int mfma_tile_bm(int t) { const int v[] = {256, 128, 64, 128, 64}; return v[t]; }
 inline int mfma_tile_bn(int t) { const int v[] = {256, 128, 64, 64, 128}; return v[t]; }
+// Workgroups of the direct-to-LDS kernel that one CU holds at once, by tile
+// (LDS ring: 2 stages of 128x128 fit twice in 160 KB; the other rings fill one
+// CU; every variant runs at most 2 waves per SIMD).
+inline int mfma_dtl_wgs_per_cu(int t) { return t == T128x128 ? 2 : 1; }
 // LDS bytes: two stages of (BM + BN) rows x 128 bytes of K (+ BM FP32 row scales for FP8).
 inline int mfma_tile_lds(int t, bool fp8) {
     return 2 * ((mfma_tile_bm(t) + mfma_tile_bn(t)) * 128 + (fp8 ? mfma_tile_bm(t) * 4 : 0));

@@ -16,6 +16,7 @@ struct Overrides {
     int force_tile = -1;
     bool no_vec = false;
     bool no_dtl = false;
+    bool no_tail_split = false;
     bool log = false;
 };
 
@@ -36,6 +37,7 @@ const Overrides &overrides() {
         }
         if (const char *s = std::getenv("DG_NO_VEC")) r.no_vec = s[0] == '1';
         if (const char *s = std::getenv("DG_NO_DTL")) r.no_dtl = s[0] == '1';
+        if (const char *s = std::getenv("DG_NO_TAIL_SPLIT")) r.no_tail_split = s[0] == '1';
         if (const char *s = std::getenv("DG_LOG")) r.log = s[0] == '1';
         return r;
     }();
@@ -211,6 +213,27 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     // the direct kernel splits K only on tiles of at most 64 accumulators per lane
     if (pl.dtl && (tile == T256x256)) S = 1;
     S = std::max<int64_t>(S, 1);
+    // Tail of the last wave (direct kernel, whole tiles): when the tiles fill
+    // whole waves of workgroup slots and the tiles left over would keep at most
+    // half of the CUs busy, those tiles are split along K into pieces that
+    // spread over the idle CUs (the earlier tiles stay whole, so the split
+    // costs only on the tail).  A last wave with a tile on every CU needs no
+    // help: a CU running one workgroup instead of two runs it about twice as
+    // fast (measured on FP8 4096 x 7168, 1792 tiles = 3.5 waves of 512 slots:
+    // splitting its last 256 tiles made it slower, 189 us against 185 us).
+    pl.dp_tiles = 0;
+    if (pl.dtl && S == 1 && tile != T256x256 && overrides().force_splitk <= 0 && !overrides().no_tail_split) {
+        const int64_t nt = tile_count(p.M, p.N, tile);
+        const int64_t slots = (int64_t)d.cus * mfma_dtl_wgs_per_cu(tile);
+        const int64_t full = nt / slots, left = nt - full * slots;
+        if (full >= 1 && left > 0 && 2 * left <= d.cus) {
+            const int64_t St = std::min<int64_t>(d.cus / left, pl.ktiles / 8);
+            if (St >= 2) {
+                S = St;
+                pl.dp_tiles = (int)(full * slots);
+            }
+        }
+    }
     pl.kt_per_split = (int)cdiv(std::max(pl.ktiles, 1), S);
     pl.splits = (int)cdiv(std::max(pl.ktiles, 1), pl.kt_per_split);
     // tile raster: a group of tile rows walked together (measured on the
@@ -218,6 +241,10 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     pl.group_m = std::min(pl.tiles_m, tile == T128x128 ? 8 : 4);
     pl.lds_bytes = mfma_tile_lds(pl.slow ? T64x64 : tile, p.fp8);
     pl.counters = pl.dtl && pl.splits > 1 ? pl.tiles_m * pl.tiles_n : 0;
+    // the direct kernel's partials: one BM x BN tile per piece of each split tile
+    if (pl.dtl && pl.splits > 1)
+        pl.ws_bytes = (size_t)(pl.tiles_m * pl.tiles_n - pl.dp_tiles) * (size_t)pl.splits *
+                      (size_t)mfma_tile_bm(tile) * (size_t)mfma_tile_bn(tile) * sizeof(float);
 }
 
 }  // namespace
@@ -233,7 +260,8 @@ Plan select_plan(const Problem &p, const Device &d) {
         pl = Plan();
         plan_mfma(p, pl, d);
     }
-    pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
+    if (!(pl.path == Path::Mfma && pl.dtl))
+        pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
     return pl;
 }
 
@@ -304,11 +332,13 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
         break;
     case Path::Mfma:
         add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d dtl=%d tiles=%dx%d ktiles=%d splits=%d "
-            "kt_per_split=%d group_m=%d grid=%dx1x%d lds=%d",
+            "kt_per_split=%d dp_tiles=%d group_m=%d grid=%dx1x%d lds=%d",
             mfma_tile_bm(pl.slow ? T64x64 : pl.tile), mfma_tile_bn(pl.slow ? T64x64 : pl.tile),
             modes[pl.a.mode], modes[pl.b.mode], (int)pl.a.vec, (int)pl.b.vec, pl.slow, pl.dtl, pl.tiles_m,
-            pl.tiles_n, pl.ktiles, pl.splits, pl.kt_per_split, pl.group_m, pl.tiles_m * pl.tiles_n,
-            pl.splits, pl.lds_bytes);
+            pl.tiles_n, pl.ktiles, pl.splits, pl.kt_per_split, pl.dp_tiles, pl.group_m,
+            pl.dtl && pl.splits > 1 ? pl.dp_tiles + (pl.tiles_m * pl.tiles_n - pl.dp_tiles) * pl.splits
+                                    : pl.tiles_m * pl.tiles_n,
+            pl.dtl ? 1 : pl.splits, pl.lds_bytes);
         break;
     }
     add(" ws=%zu", pl.ws_bytes);

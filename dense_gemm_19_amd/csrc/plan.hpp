@@ -56,6 +56,7 @@ struct Plan {
     int slow = 0;
     int dtl = 0;              // direct HBM -> LDS kernel (gemm_dtl.hip)
     int tiles_m = 0, tiles_n = 0, ktiles = 0, kt_per_split = 0, group_m = 1;
+    int dp_tiles = 0;         // direct kernel with splits: tiles run whole before the split ones
     // streaming path
     int sk_kind = SK_BN, sk_mmax = 1, sk_grid_x = 0, sk_k_per_split = 0, sk_a_vec = 0;
     int sk_kc = 0;            // SK_BN: A rows staged in LDS per chunk
@@ -69,8 +70,9 @@ struct Plan {
 
 // Choose the plan for a validated problem.  Honors DG_FORCE_PATH=skinny|mfma,
 // DG_FORCE_SPLITK=<n>, DG_FORCE_TILE=<256x256|128x128|64x64|128x64> and
-// DG_NO_VEC=1 (element-wise loads everywhere) and DG_NO_DTL=1 (register-staged
-// tile loads only), read once per process.
+// DG_NO_VEC=1 (element-wise loads everywhere), DG_NO_DTL=1 (register-staged
+// tile loads only) and DG_NO_TAIL_SPLIT=1 (no split of the last wave's tiles),
+// read once per process.
 Plan select_plan(const Problem &p, const Device &d);
 
 // Same as select_plan, through a mutex-guarded cache keyed by everything the

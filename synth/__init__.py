@@ -268,6 +268,10 @@ def config(name: str) -> Case:
         return fp8_case(128, 7168, 4096, seed=106, name="c5_128")
     if name == "c5_4096":
         return fp8_case(4096, 7168, 4096, seed=107, name="c5_4096")
+    if name == "c5_tail":
+        # FP8 4096 x 4224 x 4096: 1056 tiles of 128 x 128, two whole waves of 512
+        # workgroup slots and 32 tiles over (a shape with a short last wave)
+        return fp8_case(4096, 4224, 4096, seed=109, name="c5_tail")
     if name.endswith("_gelu") and name[:-5] in CONFIGS:
         # the same operands, then a BF16 bias N(0,1) from rng(seed 201) and GELU
         return with_epilogue(config(name[:-5]), "gelu_tanh", torch.bfloat16, "contig", seed=201,

@@ -247,3 +247,50 @@ def test_dtl_tiles(dg, kind, layouts, shape):
     dtl, text = _plan_field(dg, c, "dtl")
     assert dtl == "1", text
     check(dg, c, rows=_sample_rows(M, seed=seed))
+
+
+# ---------------------------------------------------------------- the split tail of the last wave
+
+TAIL_CASES = [
+    ("fp8", 2512, 3312, 2048, "row"),      # 520 tiles of 128x128: 512 whole, 8 split in 2
+    ("fp8", 2512, 3312, 2048, "col"),
+    ("bf16", 2900, 2904, 2048, "row"),     # 529 tiles: 512 whole, 17 split in 4, ragged edges
+    ("f16", 2900, 2904, 1024, "row"),      # 17 split in 2, beta = 1 and an FP32 C
+]
+
+
+@pytest.mark.parametrize("tc", TAIL_CASES, ids=lambda t: f"{t[0]}-{t[1]}x{t[2]}x{t[3]}-B{t[4]}")
+def test_tail_split(dg, tc):
+    kind, M, N, K, bl = tc
+    if kind == "fp8":
+        c = synth.fp8_case(M, N, K, seed=M + K, b_layout=bl, out_dtype=torch.float32, beta=0.5)
+    else:
+        c = synth.gemm_case(M, N, K, F16 if kind == "f16" else BF16, torch.float32 if kind == "f16" else BF16,
+                            seed=N + K, b_layout=bl, beta=1.0 if kind == "f16" else 0.0)
+    dp, text = _plan_field(dg, c, "dp_tiles")
+    assert int(dp) == 512 and "splits=1 " not in text, text
+    # rows from the whole tiles and from the split ones (the raster's last tiles)
+    rows = sorted(set([0, 1, 127, 128, 1000, M // 2] + list(range(M - 130, M, 7)) + [M - 1]))
+    check(dg, c, rows=rows)
+
+
+def test_tail_split_integer_bitwise_and_repeatable(dg):
+    g = synth.rng(91)
+    M, N, K = 2512, 3312, 2048
+    A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), torch.float32).to(E4M3)
+    B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), torch.float32).to(E4M3)
+    c = synth.Case("int_tail", A, B, torch.zeros(M, N), 1.0, 0.0, torch.ones(M, K // 128),
+                   torch.ones(K // 128, -(-N // 128)), rtol=1e-3)
+    assert int(_plan_field(dg, c, "dp_tiles")[0]) == 512
+    check(dg, c, rows=list(range(0, M, 97)) + list(range(M - 16, M)), expect_bitwise=True)
+    d1 = run_case(dg, c).C.cpu()
+    d2 = run_case(dg, c).C.cpu()
+    assert torch.equal(d1, d2)
+
+
+def test_tail_split_workload_c5_tail(dg):
+    case = synth.config("c5_tail")      # FP8 4096 x 4224 x 4096: 1024 whole tiles, 32 split in 4
+    dp, text = _plan_field(dg, case, "dp_tiles")
+    assert int(dp) == 1024, text
+    M = case.mnk[0]
+    check(dg, case, rows=_sample_rows(M, seed=5) + list(range(M - 200, M, 9)))
