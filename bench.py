@@ -32,7 +32,10 @@ The JSON line also carries:
                 token, q_b: B per 128x128 block; GB/s against HBM peak), and
                 the fused bias + GELU epilogue on three of the GEMMs (*_gelu:
                 vs_plain_us is its cost over the plain GEMM, unfused_floor_us
-                the least a separate bias + GELU pass over C would take), and
+                the least a separate bias + GELU pass over C would take),
+                each GEMM config's `tuned` record (dg_gemm_tune's choice among
+                its candidate plans, timed again over the rotated buffers,
+                with the tuning time and the calls that pay it back), and
                 moe8: the 8 MoE expert GEMMs [1,512] x [512,4096] in one
                 dg_gemm_grouped call, against the same GEMMs as 8 dg_gemm calls.
 """
@@ -180,8 +183,7 @@ def time_quant(dg, name, trials=5):
     calls = [QuantCall(dg, x, q, sc, mode, stream) for x, q, sc in sets]
     nbytes = M * K * 2 + M * K + nsc * 4
     reps = max(20, min(2000, int(2e-3 / max(nbytes / 6e12, 2e-6))))
-    run_checked(calls, range(10))
-    torch.cuda.synchronize()
+    warm(calls)
     times = []
     for _ in range(trials):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -236,8 +238,7 @@ def time_grouped(dg, trials=5):
 
     def timed(calls, per_step):
         reps = 200
-        run_checked(calls, range(10 * per_step))
-        torch.cuda.synchronize()
+        warm(calls)
         ts = []
         for _ in range(trials):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -280,18 +281,30 @@ def run_checked(calls, idx):
 
 # ---------------------------------------------------------------- timing
 
-def time_config(dg, name, reps=None, trials=5):
-    """Per-launch time of one workload over rotated buffer sets (median of trials)."""
+WARM_MS = 150.0   # sustained work before any timed region (the clocks ramp up over ~30 ms)
+
+
+def warm(calls, ms=WARM_MS):
+    """Run the calls back to back for about `ms` milliseconds: under sustained
+    load the same kernel runs up to ~12 % faster than in its first
+    milliseconds (BF16 4096^3: 141 us per launch in the first 20 launches,
+    110 us after ~30 ms), and every timed region should see the steady state."""
     import torch
-    import synth
-    case = synth.config(name)
-    sets = rotated_sets(case, "cuda:0")
-    calls = prepared(dg, sets)
-    nbytes, flops = algorithmic(case)
-    if reps is None:   # aim for a few ms per trial
-        reps = max(20, min(2000, int(2e-3 / max(flops / 2e15, nbytes / 6e12, 2e-6))))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
     run_checked(calls, range(10))
+    e1.record()
+    e1.synchronize()
+    per = max(e0.elapsed_time(e1) / 10, 1e-3)
+    run_checked(calls, range(int(ms / per) + 1))
     torch.cuda.synchronize()
+
+
+def time_calls(calls, reps, trials):
+    """Median and minimum per-launch time of `reps` launches between two events."""
+    import torch
+    warm(calls)
     per = []
     for _ in range(trials):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -302,7 +315,23 @@ def time_config(dg, name, reps=None, trials=5):
         e1.synchronize()
         per.append(e0.elapsed_time(e1) * 1e-3 / reps)
     per.sort()
-    t = per[len(per) // 2]
+    return per[len(per) // 2], per[0]
+
+
+def time_config(dg, name, reps=None, trials=5, tune=False):
+    """Per-launch time of one workload over rotated buffer sets (median of
+    trials); with tune, the problem is then tuned (dg_gemm_tune on the first
+    buffer set) and timed again the same way with the tuned plan."""
+    import torch
+    import synth
+    case = synth.config(name)
+    sets = rotated_sets(case, "cuda:0")
+    calls = prepared(dg, sets)
+    nbytes, flops = algorithmic(case)
+    if reps is None:   # aim for a few ms per trial
+        reps = max(20, min(2000, int(2e-3 / max(flops / 2e15, nbytes / 6e12, 2e-6))))
+    t, t_min = time_calls(calls, reps, trials)
+    per = [t_min]
     M = case.mnk[0]
     plan = dg.plan(sets[0].A, sets[0].B, sets[0].C, case.alpha, case.beta, sets[0].A_scale,
                    sets[0].B_scale)
@@ -323,6 +352,17 @@ def time_config(dg, name, reps=None, trials=5):
     if case.fused:
         rec["epilogue"] = f"+bias({str(case.bias.dtype).split('.')[-1]}) {case.act}" if case.bias is not None \
             else case.act
+    if tune:
+        s0 = sets[0]
+        r = dg.tune(s0.A, s0.B, s0.C, s0.A_scale, s0.B_scale, reps=3)
+        tt, tt_min = time_calls(calls, reps, trials)
+        rec["tuned"] = {"us": round(tt * 1e6, 3), "us_min": round(tt_min * 1e6, 3),
+                        "speedup": round(t / tt, 4), "tune_ms": round(r["tune_ms"], 2),
+                        "candidates": r["candidates"], "chosen": r["chosen"],
+                        "tuner_default_us": round(r["default_us"], 3), "tuner_best_us": round(r["best_us"], 3),
+                        "plan": r["plan"].split(" | ")[0].split(" path=")[1],
+                        "calls_to_amortize": (round(r["tune_ms"] * 1e-3 / (t - tt)) if tt < t else None)}
+        dg.tune_clear()
     del sets
     torch.cuda.empty_cache()
     return rec
@@ -404,7 +444,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
+    # (5000 steps of ~26 us: the clocks reach their sustained state before timing)
+    ap.add_argument("--warmup", type=int, default=5000)
     ap.add_argument("--configs", default="all",
                     help="other workloads to time: all, none, or a comma list of "
                          "c1,c3,c4,c5_128,c5_4096,c5_tail (GEMMs), <config>_gelu (the same GEMM with a "
@@ -413,6 +454,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip tuning the GEMM configs (dg_gemm_tune, then a second timing with the tuned plan)")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip the measured peaks (register-only MFMA loops, 2 GiB read, launch floor)")
     args = ap.parse_args()
@@ -495,7 +538,7 @@ def main():
         if args.configs == "all" else args.configs.split(","))
     for n in names:
         others[n] = (time_quant(dg, n) if n in QUANT_CONFIGS else time_grouped(dg) if n == "moe8"
-                     else time_config(dg, n))
+                     else time_config(dg, n, tune=not args.no_tune and not n.endswith("_gelu")))
         log(n, json.dumps(others[n]))
     # fused epilogue: its cost over the plain GEMM of the same operands, and the
     # least a separate bias + GELU pass would add (read C and write it again

@@ -50,6 +50,21 @@ class View(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class PlanChoice(ctypes.Structure):
+    """dg_plan_choice: path (0 built-in, 1 streaming, 2 matrix-core), tile (-1 or a
+    tile index), splits (0 built-in), tail (-1 built-in, 0 no tail split)."""
+    _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("tail", ctypes.c_int32)]
+
+    def astuple(self):
+        return (self.path, self.tile, self.splits, self.tail)
+
+
+class TuneResult(ctypes.Structure):
+    _fields_ = [("default_us", ctypes.c_double), ("best_us", ctypes.c_double), ("tune_ms", ctypes.c_double),
+                ("candidates", ctypes.c_int32), ("chosen", ctypes.c_int32), ("plan", ctypes.c_char * 512)]
+
+
 _lib = None
 
 
@@ -72,6 +87,16 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_void_p]
         L.dg_gemm_fp8_epilogue.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_void_p]
+        PC = ctypes.POINTER(PlanChoice)
+        L.dg_gemm_candidates.argtypes = [P, P, P, P, P, PC, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+        L.dg_gemm_with_choice.argtypes = [P, P, P, P, P, PC, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_tune.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.POINTER(TuneResult), ctypes.c_void_p]
+        L.dg_tune_save.argtypes = [ctypes.c_char_p]
+        L.dg_tune_load.argtypes = [ctypes.c_char_p]
+        for f in ("dg_gemm_candidates", "dg_gemm_with_choice", "dg_gemm_tune", "dg_tune_save", "dg_tune_load"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dg_tune_clear.restype = None
+        L.dg_tune_count.restype = ctypes.c_int32
         L.dg_gemm_grouped.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
         L.dg_gemm_grouped_plan.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_char_p, ctypes.c_size_t]
@@ -201,6 +226,55 @@ def grouped_plan(As, Bs, Cs, alpha: float = 1.0, beta: float = 0.0) -> str:
     st, text = grouped_plan_views(len(As), _view_array(As), _view_array(Bs), _view_array(Cs), alpha, beta)
     _check(st, "dg_gemm_grouped_plan")
     return text
+
+
+def _opt_views(A, A_scale, B, B_scale, C):
+    vs = [view_of(A), None if A_scale is None else view_of(A_scale), view_of(B),
+          None if B_scale is None else view_of(B_scale), view_of(C)]
+    return vs, [ctypes.byref(v) if v is not None else None for v in vs]
+
+
+def candidates(A, B, C, A_scale=None, B_scale=None) -> list:
+    """The candidate plan choices the tuner would time, as (path, tile, splits, tail)."""
+    _, refs = _opt_views(A, A_scale, B, B_scale, C)
+    arr = (PlanChoice * 64)()
+    n = ctypes.c_int32(0)
+    _check(lib().dg_gemm_candidates(*refs, arr, 64, ctypes.byref(n)), "dg_gemm_candidates")
+    return [arr[i].astuple() for i in range(min(n.value, 64))]
+
+
+def gemm_with_choice(A, B, C, choice, alpha: float = 1.0, beta: float = 0.0, A_scale=None, B_scale=None,
+                     stream=None):
+    """dg_gemm / dg_gemm_fp8 with an explicit (path, tile, splits, tail) plan choice; returns C."""
+    vs, refs = _opt_views(A, A_scale, B, B_scale, C)
+    c = PlanChoice(*choice)
+    _check(lib().dg_gemm_with_choice(*refs, ctypes.byref(c), alpha, beta, _stream(stream)), "dg_gemm_with_choice")
+    return C
+
+
+def tune(A, B, C, A_scale=None, B_scale=None, reps: int = 0, stream=None) -> dict:
+    """Time the candidate plans of this problem (C is overwritten), keep the fastest."""
+    vs, refs = _opt_views(A, A_scale, B, B_scale, C)
+    r = TuneResult()
+    _check(lib().dg_gemm_tune(*refs, reps, ctypes.byref(r), _stream(stream)), "dg_gemm_tune")
+    return {"default_us": r.default_us, "best_us": r.best_us, "tune_ms": r.tune_ms,
+            "candidates": r.candidates, "chosen": r.chosen, "plan": r.plan.decode()}
+
+
+def tune_save(path: str):
+    _check(lib().dg_tune_save(os.fsencode(path)), "dg_tune_save")
+
+
+def tune_load(path: str):
+    _check(lib().dg_tune_load(os.fsencode(path)), "dg_tune_load")
+
+
+def tune_clear():
+    lib().dg_tune_clear()
+
+
+def tune_count() -> int:
+    return lib().dg_tune_count()
 
 
 def plan_views(A: View, B: View, C: View, alpha: float = 1.0, beta: float = 0.0,

@@ -5,7 +5,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
 #include <unordered_map>
+#include <vector>
 
 namespace dg {
 namespace {
@@ -76,7 +78,7 @@ OperandPlan plan_b(const Mat &B, int64_t N, int64_t K, int epc) {
     return o;
 }
 
-bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
+bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c) {
     if (p.fp8 || p.M > 8) return false;
     const Mat &A = p.A, &B = p.B;
     const int mmax = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
@@ -94,6 +96,7 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
         const int64_t sweeps = cdiv(std::max<int64_t>(p.K, 1), sweep);
         int64_t S = std::max<int64_t>(1, std::min<int64_t>(d.cus / pl.sk_grid_x, sweeps / 2));
         if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, sweeps);
+        if (c.splits > 0) S = std::min<int64_t>(c.splits, sweeps);
         // splits and LDS chunks are whole sweeps (only the last sweep of K is partial)
         const int64_t kps = cdiv(sweeps, S) * sweep;
         pl.sk_k_per_split = (int)kps;
@@ -113,6 +116,7 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d) {
         pl.sk_grid_x = (int)cdiv(p.N, pl.sk_waves);
         int64_t S = 1;
         if (overrides().force_splitk > 0) S = overrides().force_splitk;
+        if (c.splits > 0) S = c.splits;
         int64_t kps = cdiv(cdiv(std::max<int64_t>(p.K, 1), S), 8) * 8;
         pl.sk_k_per_split = (int)kps;
         pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
@@ -134,7 +138,7 @@ int64_t tile_count(int64_t M, int64_t N, int t) {
     return cdiv(M, mfma_tile_bm(t)) * cdiv(N, mfma_tile_bn(t));
 }
 
-void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
+void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c) {
     const int epc = p.fp8 ? 16 : 8;              // elements per 16-byte chunk
     const int kel = p.fp8 ? 128 : 64;            // K elements per tile
     pl.path = Path::Mfma;
@@ -152,8 +156,8 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     const bool b_fits = 255 * pl.b.r_stride + (kel - 1) * pl.b.k_stride + 16 < lim;
     const bool s_fits = !p.fp8 || ((p.M - 1) * p.SA.rs + 4 < lim && (cdiv(p.N, 128) - 1) * p.SB.cs + 4 < lim);
     pl.dtl = !pl.slow && p.K % kel == 0 && a_fits && b_fits && s_fits && !overrides().no_dtl;
+    // Tile: the heuristic below, or the caller's choice where the kernel has it.
     int tile = T64x64;
-    int64_t S = 1;
     if (pl.dtl) {
         if (p.M <= 128) {
             // Few rows: the shape is bound by streaming B, and the work is split
@@ -165,28 +169,22 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
             // a ticket, partials read back by the last workgroup).
             tile = p.fp8 ? T64x128 : T64x64;
             if (p.M > 64 && !p.fp8 && tile_eff(p.M, p.N, T128x64) > tile_eff(p.M, p.N, tile) + 1e-9) tile = T128x64;
-            const int64_t nt = tile_count(p.M, p.N, tile);
-            S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 16));
         } else {
             // Enough rows for a compute-bound shape: the largest tile (FP8 stops at
             // 128x128, whose promotion fits the registers) that still gives every
-            // CU a tile, else the one giving the most tiles; no split.
+            // CU a tile, else the one giving the most tiles.
             const int order[] = {T256x256, T128x128, T128x64, T64x64};
             int64_t best_tiles = -1;
-            bool found = false;
             for (int t : order) {
                 if (p.fp8 && t == T256x256) continue;
                 if (tile_eff(p.M, p.N, t) < 0.75 && t != T64x64) continue;
                 const int64_t nt = tile_count(p.M, p.N, t);
-                if (nt >= d.cus) { tile = t; found = true; break; }
+                if (nt >= d.cus) { tile = t; break; }
                 if (nt > best_tiles) { best_tiles = nt; tile = t; }
             }
-            (void)found;
-            const int64_t nt = tile_count(p.M, p.N, tile);
-            if (nt < d.cus && tile != T256x256 && tile != T128x128)
-                S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 8));
         }
         if (overrides().force_tile >= 0) tile = overrides().force_tile;
+        if (c.tile >= 0 && !(p.fp8 && c.tile == T256x256)) tile = c.tile;
     } else if (!pl.slow) {
         // general kernel (register-staged loads, K tails): tiles it implements
         const int order[] = {T256x256, T128x128, T128x64, T64x64};
@@ -202,7 +200,16 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
         }
         if (!found) tile = best;
         if (overrides().force_tile >= 0 && overrides().force_tile != T64x128) tile = overrides().force_tile;
-        const int64_t nt = tile_count(p.M, p.N, tile);
+        if (c.tile >= 0 && c.tile != T64x128 && !(p.fp8 && c.tile == T256x256)) tile = c.tile;
+    }
+    // K split for that tile.
+    int64_t S = 1;
+    const int64_t nt = tile_count(p.M, p.N, tile);
+    if (pl.dtl) {
+        if (p.M <= 128) S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 16));
+        else if (nt < d.cus && tile != T256x256 && tile != T128x128)
+            S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 8));
+    } else if (!pl.slow) {
         if (nt < d.cus) S = std::min<int64_t>(cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2));
         S = std::min<int64_t>(S, 16);
     }
@@ -210,6 +217,7 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     pl.tiles_m = (int)cdiv(p.M, mfma_tile_bm(tile));
     pl.tiles_n = (int)cdiv(p.N, mfma_tile_bn(tile));
     if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, std::max(pl.ktiles, 1));
+    if (c.splits > 0) S = std::min<int64_t>(c.splits, std::max(pl.ktiles, 1));
     // the direct kernel splits K only on tiles of at most 64 accumulators per lane
     if (pl.dtl && (tile == T256x256)) S = 1;
     S = std::max<int64_t>(S, 1);
@@ -222,8 +230,8 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
     // fast (measured on FP8 4096 x 7168, 1792 tiles = 3.5 waves of 512 slots:
     // splitting its last 256 tiles made it slower, 189 us against 185 us).
     pl.dp_tiles = 0;
-    if (pl.dtl && S == 1 && tile != T256x256 && overrides().force_splitk <= 0 && !overrides().no_tail_split) {
-        const int64_t nt = tile_count(p.M, p.N, tile);
+    if (pl.dtl && S == 1 && tile != T256x256 && overrides().force_splitk <= 0 && !overrides().no_tail_split &&
+        c.splits <= 0 && c.tail != 0) {
         const int64_t slots = (int64_t)d.cus * mfma_dtl_wgs_per_cu(tile);
         const int64_t full = nt / slots, left = nt - full * slots;
         if (full >= 1 && left > 0 && 2 * left <= d.cus) {
@@ -249,16 +257,18 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d) {
 
 }  // namespace
 
-Plan select_plan(const Problem &p, const Device &d) {
+Plan select_plan(const Problem &p, const Device &d) { return select_plan(p, d, PlanChoice()); }
+
+Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c) {
     Plan pl;
     if (p.M == 0 || p.N == 0) { pl.path = Path::Noop; return pl; }
     if (p.alpha == 0.0f || p.K == 0) { pl.path = Path::Scale; return pl; }
-    const int fp = overrides().force_path;
-    if (fp != 2 && skinny_ok(p, pl, d)) {
+    const int fp = c.path ? c.path : overrides().force_path;
+    if (fp != 2 && skinny_ok(p, pl, d, c)) {
         pl.path = Path::Skinny;
     } else {
         pl = Plan();
-        plan_mfma(p, pl, d);
+        plan_mfma(p, pl, d, c);
     }
     if (!(pl.path == Path::Mfma && pl.dtl))
         pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
@@ -268,8 +278,9 @@ Plan select_plan(const Problem &p, const Device &d) {
 namespace {
 
 struct Key {
+    char arch[16];            // device architecture name up to its first ':' or ' '
     int64_t M, N, K;
-    int64_t ars, acs, brs, bcs;
+    int64_t ars, acs, brs, bcs, sars, sbcs;
     int fp8, in_kind, out_kind, scale_only;
     int aal, bal, aalr, aalc, balr, balc;
     int cus;
@@ -285,30 +296,203 @@ struct KeyHash {
     }
 };
 
-}  // namespace
-
-Plan cached_plan(const Problem &p, const Device &d) {
+Key make_key(const Problem &p, const Device &d) {
     Key k;
     std::memset(&k, 0, sizeof k);
+    for (int i = 0; i < 15 && d.arch[i] && d.arch[i] != ':' && d.arch[i] != ' '; ++i) k.arch[i] = d.arch[i];
     k.M = p.M; k.N = p.N; k.K = p.K;
     k.ars = p.A.rs; k.acs = p.A.cs; k.brs = p.B.rs; k.bcs = p.B.cs;
+    k.sars = p.fp8 ? p.SA.rs : 0; k.sbcs = p.fp8 ? p.SB.cs : 0;
     k.fp8 = p.fp8; k.in_kind = p.in_kind; k.out_kind = p.out_kind;
     k.scale_only = (p.alpha == 0.0f);
     k.aal = p.A.align_ptr; k.bal = p.B.align_ptr;
     k.aalr = p.A.align_rs; k.aalc = p.A.align_cs; k.balr = p.B.align_rs; k.balc = p.B.align_cs;
     k.cus = d.cus;
-    static std::mutex mu;
-    static std::unordered_map<Key, Plan, KeyHash> cache;
+    return k;
+}
+
+// The plan cache and the tuned choices, under one mutex (a tuned choice
+// replaces the cached plan of its key).
+struct Tables {
+    std::mutex mu;
+    std::unordered_map<Key, Plan, KeyHash> plans;
+    std::unordered_map<Key, PlanChoice, KeyHash> tuned;
+};
+
+Tables &tables() {
+    static Tables t;
+    return t;
+}
+
+}  // namespace
+
+Plan cached_plan(const Problem &p, const Device &d) {
+    const Key k = make_key(p, d);
+    Tables &t = tables();
+    PlanChoice c;
     {
-        std::lock_guard<std::mutex> g(mu);
-        auto it = cache.find(k);
-        if (it != cache.end()) return it->second;
+        std::lock_guard<std::mutex> g(t.mu);
+        auto it = t.plans.find(k);
+        if (it != t.plans.end()) return it->second;
+        auto tc = t.tuned.find(k);
+        if (tc != t.tuned.end()) c = tc->second;
     }
-    Plan pl = select_plan(p, d);
-    std::lock_guard<std::mutex> g(mu);
-    auto ins = cache.emplace(k, pl);
+    Plan pl = select_plan(p, d, c);
+    std::lock_guard<std::mutex> g(t.mu);
+    auto ins = t.plans.emplace(k, pl);
     if (ins.second && overrides().log) std::fprintf(stderr, "[dg] %s\n", describe(p, pl, d).c_str());
     return ins.first->second;
+}
+
+Plan tuned_or_selected(const Problem &p, const Device &d) {
+    const Key k = make_key(p, d);
+    Tables &t = tables();
+    PlanChoice c;
+    {
+        std::lock_guard<std::mutex> g(t.mu);
+        auto tc = t.tuned.find(k);
+        if (tc != t.tuned.end()) c = tc->second;
+    }
+    return select_plan(p, d, c);
+}
+
+void tune_store(const Problem &p, const Device &d, const PlanChoice &c) {
+    const Key k = make_key(p, d);
+    Tables &t = tables();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.tuned[k] = c;
+    t.plans.erase(k);
+}
+
+void tune_clear() {
+    Tables &t = tables();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.tuned.clear();
+    t.plans.clear();
+}
+
+int tune_count() {
+    Tables &t = tables();
+    std::lock_guard<std::mutex> g(t.mu);
+    return (int)t.tuned.size();
+}
+
+// One line per entry:
+//   dgtune1 <arch> <cus> <M> <N> <K> <ars> <acs> <brs> <bcs> <sars> <sbcs> <fp8> <in> <out>
+//           <scale_only> <aal> <bal> <aalr> <aalc> <balr> <balc> <path> <tile> <splits> <tail>
+bool tune_save(const char *path) {
+    Tables &t = tables();
+    std::lock_guard<std::mutex> g(t.mu);
+    FILE *f = std::fopen(path, "w");
+    if (!f) return false;
+    bool ok = std::fprintf(f, "# dense GEMM tuned plans: key fields, then path tile splits tail\n") > 0;
+    for (const auto &e : t.tuned) {
+        const Key &k = e.first;
+        const PlanChoice &c = e.second;
+        ok = ok && std::fprintf(f,
+                                "dgtune1 %s %d %lld %lld %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %d %d "
+                                "%d %d %d %d\n",
+                                k.arch[0] ? k.arch : "-", k.cus, (long long)k.M, (long long)k.N, (long long)k.K,
+                                (long long)k.ars, (long long)k.acs, (long long)k.brs, (long long)k.bcs,
+                                (long long)k.sars, (long long)k.sbcs, k.fp8, k.in_kind, k.out_kind, k.scale_only,
+                                k.aal, k.bal, k.aalr, k.aalc, k.balr, k.balc, c.path, c.tile, c.splits, c.tail) > 0;
+    }
+    return std::fclose(f) == 0 && ok;
+}
+
+bool tune_load(const char *path) {
+    FILE *f = std::fopen(path, "r");
+    if (!f) return false;
+    std::vector<std::pair<Key, PlanChoice>> got;
+    char line[1024];
+    bool ok = true;
+    while (std::fgets(line, sizeof line, f)) {
+        if (line[0] == '#' || line[0] == '\n') continue;
+        Key k;
+        std::memset(&k, 0, sizeof k);
+        PlanChoice c;
+        char arch[64];
+        long long v[11];
+        int n = std::sscanf(line,
+                            "dgtune1 %63s %d %lld %lld %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %d %d "
+                            "%d %d %d %d",
+                            arch, &k.cus, &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7], &v[8], &k.fp8,
+                            &k.in_kind, &k.out_kind, &k.scale_only, &k.aal, &k.bal, &k.aalr, &k.aalc, &k.balr,
+                            &k.balc, &c.path, &c.tile, &c.splits, &c.tail);
+        if (n != 25 || c.path < 0 || c.path > 2 || c.tile < -1 || c.tile >= NUM_MFMA_TILES || c.splits < 0 ||
+            c.splits > 64) {
+            ok = false;
+            break;
+        }
+        if (std::strcmp(arch, "-") != 0) std::snprintf(k.arch, sizeof k.arch, "%.15s", arch);
+        k.M = v[0]; k.N = v[1]; k.K = v[2]; k.ars = v[3]; k.acs = v[4]; k.brs = v[5]; k.bcs = v[6];
+        k.sars = v[7]; k.sbcs = v[8];
+        got.emplace_back(k, c);
+    }
+    std::fclose(f);
+    if (!ok) return false;   // nothing from a malformed file is used
+    Tables &t = tables();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (const auto &e : got) {
+        t.tuned[e.first] = e.second;
+        t.plans.erase(e.first);
+    }
+    return true;
+}
+
+std::vector<PlanChoice> candidate_choices(const Problem &p, const Device &d) {
+    std::vector<PlanChoice> out;
+    std::vector<std::string> seen;
+    auto add = [&](const PlanChoice &c) {
+        const std::string s = describe(p, select_plan(p, d, c), d);
+        for (const std::string &x : seen)
+            if (x == s) return;
+        seen.push_back(s);
+        out.push_back(c);
+    };
+    add(PlanChoice());   // the built-in selection
+    const Plan def = select_plan(p, d);
+    if (def.path == Path::Skinny) {
+        for (int S : {1, 2, 3, 4, 6, 8, 12, 16}) {
+            PlanChoice c;
+            c.path = 1;
+            c.splits = S;
+            add(c);
+        }
+    } else if (def.path == Path::Mfma) {
+        std::vector<int> tiles;
+        if (def.dtl) tiles = {T256x256, T128x128, T128x64, T64x64, T64x128};
+        else if (!def.slow) tiles = {T256x256, T128x128, T128x64, T64x64};
+        else tiles = {-1};
+        for (int t : tiles) {
+            if (t >= 0 && p.fp8 && t == T256x256) continue;
+            // no tile larger than the matrix in either dimension
+            if (t >= 0 && (mfma_tile_bm(t) > std::max<int64_t>(64, p.M) || mfma_tile_bn(t) > std::max<int64_t>(64, p.N)))
+                continue;
+            PlanChoice c;
+            c.path = 2;
+            c.tile = t;
+            add(c);
+            // K splits only where the tile's grid holds fewer than two waves of
+            // workgroup slots (a fuller grid has parallelism to spare)
+            const int64_t nt = tile_count(p.M, p.N, t >= 0 ? t : T64x64);
+            if (nt >= 2 * (int64_t)d.cus * mfma_dtl_wgs_per_cu(t >= 0 ? t : T64x64)) continue;
+            for (int S : {1, 2, 4, 8}) {
+                c.splits = S;
+                c.tail = 0;
+                add(c);
+            }
+        }
+    }
+    return out;
+}
+
+std::string describe_choice(const PlanChoice &c) {
+    char b[128];
+    std::snprintf(b, sizeof b, "path=%d tile=%s splits=%d tail=%d", c.path,
+                  c.tile < 0 ? "auto" : (std::to_string(mfma_tile_bm(c.tile)) + "x" + std::to_string(mfma_tile_bn(c.tile))).c_str(),
+                  c.splits, c.tail);
+    return b;
 }
 
 std::string describe(const Problem &p, const Plan &pl, const Device &d) {

@@ -12,6 +12,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 #include "view.hpp"
@@ -68,16 +69,52 @@ struct Plan {
     int lds_bytes = 0;
 };
 
+// A caller's (or the tuner's) choice among the plans the kernels implement;
+// every field left at its default keeps the built-in selection.
+struct PlanChoice {
+    int path = 0;      // 0 built-in, 1 streaming kernel if the shape allows, 2 matrix-core kernel
+    int tile = -1;     // MfmaTile, where the selected matrix-core kernel has it
+    int splits = 0;    // K splits (0: built-in); the matrix-core 256x256 direct tile never splits
+    int tail = -1;     // 0: never split the tail of the last wave
+    bool operator==(const PlanChoice &o) const {
+        return path == o.path && tile == o.tile && splits == o.splits && tail == o.tail;
+    }
+};
+
 // Choose the plan for a validated problem.  Honors DG_FORCE_PATH=skinny|mfma,
 // DG_FORCE_SPLITK=<n>, DG_FORCE_TILE=<256x256|128x128|64x64|128x64> and
 // DG_NO_VEC=1 (element-wise loads everywhere), DG_NO_DTL=1 (register-staged
 // tile loads only) and DG_NO_TAIL_SPLIT=1 (no split of the last wave's tiles),
 // read once per process.
 Plan select_plan(const Problem &p, const Device &d);
+Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c);
 
-// Same as select_plan, through a mutex-guarded cache keyed by everything the
-// selection reads.  DG_LOG=1 prints each newly cached plan to stderr.
+// The candidate set the tuner times for a problem, kept small (the tuning
+// cost must stay a small fraction of the work it speeds up): the built-in plan
+// first, then every tile the selected matrix-core kernel implements that is
+// not larger than the matrix, with its built-in K split and, where its grid
+// holds fewer than two waves of workgroup slots, 1, 2, 4 or 8 splits; for the
+// streaming kernels 1 to 16 splits.  No two candidates give the same plan.
+std::vector<PlanChoice> candidate_choices(const Problem &p, const Device &d);
+
+// Tuned plans (a choice per problem key and device), consulted by
+// cached_plan before the built-in selection.  Keys cover the device (arch
+// name and CU count), M, N, K, byte strides, alignments and dtypes.
+void tune_store(const Problem &p, const Device &d, const PlanChoice &c);
+void tune_clear();
+int tune_count();
+// Text file of the tuned plans: one line per entry, the key fields then the
+// choice.  Load keeps entries for other devices (they match no key here).
+bool tune_save(const char *path);
+bool tune_load(const char *path);
+std::string describe_choice(const PlanChoice &c);
+
+// Same as select_plan (with the tuned choice of the problem's key, if any),
+// through a mutex-guarded cache keyed by everything the selection reads.
+// DG_LOG=1 prints each newly cached plan to stderr.
 Plan cached_plan(const Problem &p, const Device &d);
+// The same plan without touching the cache (for descriptions).
+Plan tuned_or_selected(const Problem &p, const Device &d);
 
 std::string describe(const Problem &p, const Plan &pl, const Device &d);
 

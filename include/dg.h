@@ -195,12 +195,94 @@ dg_status dg_gemm_grouped_plan(int32_t G, const dg_view *A, const dg_view *B, co
                                float alpha, float beta, char *buf, size_t len);
 
 /*
+ * Plan choices and autotuning.
+ *
+ * A plan is a kernel path with its tile and K split; the library picks one per
+ * problem with a built-in heuristic.  Fixed tile sizes cannot be best for every
+ * shape, so a problem can be tuned: a small set of candidate plans is run on
+ * the device with the real shape and precision and the fastest is kept, keyed
+ * by device (architecture and CU count) and problem (M, N, K, byte strides,
+ * alignments, dtypes), and can be saved to a file so that a process does not
+ * search again at every start ("DeepGEMM deep dive" article, sheratonhq.com,
+ * section 5.3; the "DeepGEMM is not a new model" article, cf-1.com, section
+ * 5.2, probes the best tile per shape at warm-up and warns that probing only
+ * pays when amortized).  Every later dg_gemm, dg_gemm_fp8 or
+ * dg_gemm_epilogue call with the same key uses the tuned plan; its results
+ * stay within the documented bound and are bitwise reproducible per plan.
+ *
+ * These entry points take the FP8 scale views as optional: A_scale and
+ * B_scale both NULL for FP16/BF16 inputs, both given for FP8 (dg_gemm_fp8's
+ * rules); one NULL and not the other is DG_ERR_NULL.
+ */
+typedef struct {
+    int32_t path;     /* 0 built-in, 1 streaming kernel (thin shapes), 2 matrix-core kernel */
+    int32_t tile;     /* -1 built-in, else 0: 256x256, 1: 128x128, 2: 64x64, 3: 128x64, 4: 64x128
+                         (where the selected kernel has that tile; otherwise ignored) */
+    int32_t splits;   /* 0 built-in, else the number of K splits (clamped to the K tiles; the
+                         matrix-core 256x256 direct kernel never splits) */
+    int32_t tail;     /* -1 built-in, 0 never split the tail of the last wave of tiles */
+} dg_plan_choice;
+
+typedef struct {
+    double default_us;   /* average launch duration of the built-in plan */
+    double best_us;      /* ... of the chosen plan (<= default_us) */
+    double tune_ms;      /* wall time of the whole tuning call */
+    int32_t candidates;  /* plans timed */
+    int32_t chosen;      /* index of the chosen plan in dg_gemm_candidates' list */
+    char plan[512];      /* description of the chosen plan (dg_gemm_plan's format) */
+} dg_tune_result;
+
+/* The candidate plans the tuner times for this problem, built-in plan first,
+ * no two alike: up to `max` written to out[], their number to *count.  Needs
+ * no GPU (plans for a 256-CU gfx950 when no device is visible).
+ * Errors: DG_ERR_NULL (count NULL, or out NULL with max > 0, or max < 0), and
+ * the validation errors of dg_gemm / dg_gemm_fp8. */
+dg_status dg_gemm_candidates(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                             const dg_view *B_scale, const dg_view *C, dg_plan_choice *out,
+                             int32_t max, int32_t *count);
+
+/* dg_gemm / dg_gemm_fp8 with an explicit plan choice (any choice is valid: a
+ * field that the selected kernel cannot honour is ignored).  Same semantics,
+ * bound and errors, plus DG_ERR_NULL (choice NULL) and DG_ERR_INVALID_ARG
+ * (path outside 0..2, tile outside -1..4, splits outside 0..64). */
+dg_status dg_gemm_with_choice(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                              const dg_view *B_scale, const dg_view *C, const dg_plan_choice *choice,
+                              float alpha, float beta, hipStream_t stream);
+
+/* Tune this problem on the current device: run the built-in plan for about
+ * 30 ms (the clocks rise under sustained load), then time every candidate
+ * twice, each time one untimed launch and `reps` launches between two events
+ * on `stream` (reps 0: 5), keep the fastest for the problem's key (by each
+ * candidate's better time), fill *result.  C is overwritten with A*B
+ * (alpha 1, beta 0; its earlier contents are lost); A and B are only read.
+ * Synchronizes `stream`.  Problems with M, N or K equal to 0 have nothing to
+ * tune (result->candidates = 0).
+ * Errors: DG_ERR_NULL (result NULL), DG_ERR_INVALID_ARG (reps outside
+ * 0..1000), the validation errors of dg_gemm / dg_gemm_fp8, DG_ERR_HIP. */
+dg_status dg_gemm_tune(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                       const dg_view *B_scale, const dg_view *C, int32_t reps,
+                       dg_tune_result *result, hipStream_t stream);
+
+/* Write every tuned plan to a text file (one line per entry), or add the
+ * entries of such a file (a malformed file adds nothing: DG_ERR_INVALID_ARG;
+ * entries for other devices are kept and match no problem here).
+ * Errors: DG_ERR_NULL (path NULL), DG_ERR_INVALID_ARG (cannot open, write or
+ * parse the file). */
+dg_status dg_tune_save(const char *path);
+dg_status dg_tune_load(const char *path);
+/* Forget every tuned plan; later calls use the built-in selection again. */
+void dg_tune_clear(void);
+/* Number of tuned plans held. */
+int32_t dg_tune_count(void);
+
+/*
  * Validate the arguments of dg_gemm exactly as dg_gemm does and write a
  * one-line, NUL-terminated description of the chosen plan (path, tiles,
  * split-K, grid, canonical operand layouts) into buf[0..len-1], without
  * launching anything.  Needs no GPU: with no device visible it plans for a
  * 256-CU gfx950.  Returns the status dg_gemm would return before launching.
- * buf may be NULL only if len == 0.
+ * buf may be NULL only if len == 0.  A tuned plan (dg_gemm_tune,
+ * dg_tune_load) of the same key is the one described.
  */
 dg_status dg_gemm_plan(const dg_view *A, const dg_view *B, const dg_view *C,
                        float alpha, float beta, char *buf, size_t len);

@@ -327,3 +327,60 @@ def test_grouped_validation_and_plan():
     assert gp([x, x16], [Ws[0], W16], Cs[:2])[0] == "DG_ERR_DTYPE"
     assert gp([x, x], [Ws[0], mat(BASE + 0x2000000, 511, 4096, 8192, 2)], Cs[:2])[0] == "DG_ERR_SHAPE_MISMATCH"
     assert gp([x, x], Ws[:2], Cs[:2], alpha=float("nan"))[0] == "DG_ERR_NONFINITE_SCALAR"
+
+
+def test_candidates_and_tuned_plan_files(tmp_path):
+    """dg_gemm_candidates lists distinct plans, built-in first; dg_tune_load /
+    dg_tune_save / dg_tune_clear manage the tuned table, which dg_gemm_plan
+    consults (all without a GPU: plans for a 256-CU gfx950)."""
+    import ctypes
+    L = dg.lib()
+    A, B, C = ok_triplet(64, 4096, 4096)
+    arr = (dg.PlanChoice * 64)()
+    n = ctypes.c_int32(0)
+    assert L.dg_gemm_candidates(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C), arr, 64,
+                                ctypes.byref(n)) == 0
+    cands = [arr[i].astuple() for i in range(n.value)]
+    assert cands[0] == (0, -1, 0, -1) and len(set(cands)) == len(cands) and 2 <= len(cands) <= 24, cands
+    # argument errors
+    assert dg.STATUS[L.dg_gemm_candidates(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C), arr, 64,
+                                          None)] == "DG_ERR_NULL"
+    assert dg.STATUS[L.dg_gemm_candidates(ctypes.byref(A), ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(C),
+                                          arr, 64, ctypes.byref(n))] == "DG_ERR_NULL"
+    bad = dg.PlanChoice(3, -1, 0, -1)
+    assert dg.STATUS[L.dg_gemm_with_choice(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C),
+                                           ctypes.byref(bad), 1.0, 0.0, None)] == "DG_ERR_INVALID_ARG"
+    assert dg.STATUS[L.dg_gemm_with_choice(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C),
+                                           None, 1.0, 0.0, None)] == "DG_ERR_NULL"
+    assert dg.STATUS[L.dg_gemm_tune(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C), 5, None,
+                                    None)] == "DG_ERR_NULL"
+    r = dg.TuneResult()
+    assert dg.STATUS[L.dg_gemm_tune(ctypes.byref(A), None, ctypes.byref(B), None, ctypes.byref(C), -1,
+                                    ctypes.byref(r), None)] == "DG_ERR_INVALID_ARG"
+    # a tuned entry for this key (the plan's own view of the default device)
+    dg.tune_clear()
+    before = plan(A, B, C)[1]
+    assert field(before, "tile") == "64x64"
+    line = ("dgtune1 gfx950 256 64 4096 4096 8192 2 8192 2 0 0 0 1 0 0 16 16 16 2 16 2 "
+            "2 1 2 0\n")   # path 2, tile 128x128, 2 splits, no tail split
+    f = tmp_path / "tuned.txt"
+    f.write_text("# handmade\n" + line)
+    dg.tune_load(str(f))
+    assert dg.tune_count() == 1
+    after = plan(A, B, C)[1]
+    assert field(after, "tile") == "128x128" and field(after, "splits") == "2", after
+    out = tmp_path / "saved.txt"
+    dg.tune_save(str(out))
+    assert line.split() == [l for l in out.read_text().splitlines() if l.startswith("dgtune1")][0].split()
+    dg.tune_clear()
+    assert dg.tune_count() == 0 and plan(A, B, C)[1] == before
+    dg.tune_load(str(out))
+    assert plan(A, B, C)[1] == after
+    dg.tune_clear()
+    # a malformed file adds nothing; a missing one is an error
+    (tmp_path / "bad.txt").write_text(line + "dgtune1 gfx950 256 1 2 3\n")
+    with pytest.raises(dg.DGError):
+        dg.tune_load(str(tmp_path / "bad.txt"))
+    assert dg.tune_count() == 0
+    with pytest.raises(dg.DGError):
+        dg.tune_load(str(tmp_path / "missing.txt"))

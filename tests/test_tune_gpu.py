@@ -1,0 +1,116 @@
+"""GPU parity of every plan the tuner may pick (dg_gemm_with_choice over the
+candidate list of dg_gemm_candidates) and of tuned calls (dg_gemm_tune, then
+dg_gemm with the tuned plan), against the FP64 oracle with the dg_gemm bound
+|C - C_ref| <= rtol * |alpha| * S + 4 * 2^-24 * (|alpha| * S + |beta * C_in|)
++ 0.5 * ulp_out (rtol 1e-4 for FP16/BF16, 1e-3 for FP8).
+
+Shapes cover each kernel family: the streaming kernels (B N-contiguous and
+K-contiguous), the register-staged and direct-to-LDS matrix-core kernels with
+small and large M, FP8, and a shape with a split tail.
+"""
+import os
+
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F16, BF16, F32 = torch.float16, torch.bfloat16, torch.float32
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import dense_gemm_19_amd as m
+    m.lib()   # raises if the library is missing: there is no fallback
+    m.tune_clear()
+    yield m
+    m.tune_clear()
+
+
+def cases():
+    return [
+        ("thin_bn", synth.gemm_case(2, 3000, 2048, BF16, BF16, seed=1), None),
+        ("thin_bk", synth.gemm_case(3, 500, 1000, BF16, F32, seed=2, b_layout="col"), None),
+        ("general", synth.gemm_case(65, 200, 1000, F16, F32, seed=3, beta=0.5), None),
+        ("dtl_small_m", synth.gemm_case(64, 2048, 2048, F16, F32, seed=4), None),
+        ("dtl_mid", synth.gemm_case(512, 640, 512, BF16, BF16, seed=5, alpha=1.5), None),
+        ("fp8_small_m", synth.fp8_case(128, 1024, 1024, seed=6), None),
+        ("fp8_mid", synth.fp8_case(256, 512, 1024, seed=7, out_dtype=F32, beta=0.5), None),
+        ("tail", synth.fp8_case(2512, 3312, 2048, seed=8), [0, 1, 255, 256, 1024] + list(range(2400, 2512, 8))),
+    ]
+
+
+def check(case, C, rows=None):
+    ref = oracle.ref_gemm(case.A, case.B, case.C if case.beta != 0 else None, case.alpha, case.beta, rows=rows,
+                          A_scale=case.A_scale, B_scale=case.B_scale)
+    got = C.cpu()[torch.as_tensor(ref.rows)]
+    rep = oracle.compare(got, ref, oracle.fmt_of(case.C.dtype), case.rtol)
+    return rep
+
+
+@pytest.mark.parametrize("idx", range(8), ids=[c[0] for c in cases()])
+def test_every_candidate_plan(dg, idx):
+    name, case, rows = cases()[idx]
+    cands = dg.candidates(case.A, case.B, case.C, case.A_scale, case.B_scale)
+    assert cands[0] == (0, -1, 0, -1)
+    for ch in cands:
+        d = case.to(DEV)
+        print(f"[tune] {name} {case.mnk} choice={ch} | "
+              f"{dg.plan(d.A, d.B, d.C, case.alpha, case.beta, d.A_scale, d.B_scale).split(' | ')[0]}", flush=True)
+        dg.gemm_with_choice(d.A, d.B, d.C, ch, case.alpha, case.beta, d.A_scale, d.B_scale)
+        torch.cuda.synchronize()
+        rep = check(case, d.C, rows)
+        print(f"[tune] {name} choice={ch}: {rep}", flush=True)
+        assert rep.ok, f"{name} {ch}: {rep}"
+
+
+@pytest.mark.parametrize("idx", [0, 2, 4, 6, 7], ids=lambda i: cases()[i][0])
+def test_tune_then_call(dg, idx, tmp_path):
+    name, case, rows = cases()[idx]
+    d = case.to(DEV)
+    r = dg.tune(d.A, d.B, d.C, d.A_scale, d.B_scale, reps=3)
+    print(f"[tune] {name}: {r}", flush=True)
+    assert r["candidates"] >= 1 and 0 <= r["chosen"] < r["candidates"]
+    assert r["best_us"] <= r["default_us"] + 1e-9
+    # the tuned plan is the one described and the one dg_gemm runs
+    d = case.to(DEV)
+    text = dg.plan(d.A, d.B, d.C, case.alpha, case.beta, d.A_scale, d.B_scale)
+    assert text.split(" | ")[0].split(" path=")[1] == r["plan"].split(" | ")[0].split(" path=")[1], (text, r["plan"])
+    if case.fp8:
+        dg.gemm_fp8(d.A, d.A_scale, d.B, d.B_scale, d.C, case.alpha, case.beta)
+    else:
+        dg.gemm(d.A, d.B, d.C, case.alpha, case.beta)
+    torch.cuda.synchronize()
+    rep = check(case, d.C, rows)
+    assert rep.ok, str(rep)
+    # saved, cleared, loaded: the same plan again
+    path = str(tmp_path / "tuned.txt")
+    dg.tune_save(path)
+    n = dg.tune_count()
+    dg.tune_clear()
+    assert dg.tune_count() == 0
+    dg.tune_load(path)
+    assert dg.tune_count() == n
+    assert dg.plan(d.A, d.B, d.C, case.alpha, case.beta, d.A_scale, d.B_scale) == text
+
+
+def test_tune_degenerate_and_tuned_epilogue(dg):
+    # K = 0: nothing to tune
+    c = synth.gemm_case(8, 16, 0, BF16, F32, seed=1)
+    d = c.to(DEV)
+    assert dg.tune(d.A, d.B, d.C)["candidates"] == 0
+    # a tuned key also serves the fused-epilogue entry point
+    c = synth.gemm_case(64, 2048, 2048, F16, F32, seed=4)
+    d = c.to(DEV)
+    dg.tune(d.A, d.B, d.C, reps=2)
+    e = synth.with_epilogue(c, "gelu_tanh", F32, "contig", seed=3)
+    d = e.to(DEV)
+    dg.gemm_epilogue(d.A, d.B, d.C, d.bias, dg.DG_ACT_GELU_TANH)
+    torch.cuda.synchronize()
+    from oracle import epilogue as E
+    ref = E.ref_epilogue(oracle.ref_gemm(e.A, e.B), e.bias, e.act)
+    assert E.compare_epilogue(d.C.cpu(), ref, "f32", 1e-4).ok
