@@ -441,33 +441,63 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
     const Epilogue &ep = p.epi;
     // FUSED: bias (read once per column) and activation after alpha/beta.
-    auto store = [&](auto OUTK, auto FUSED, int m, int n, float a, float bias) __attribute__((always_inline)) {
-        constexpr int ok = decltype(OUTK)::value;
-        char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
+    // The value stored at (m, n): alpha * acc (+ beta * C_in) (+ bias), activated;
+    // cin is C_in, loaded beforehand (used only when beta != 0).
+    auto value = [&](auto FUSED, float a, float bias, float cin) __attribute__((always_inline)) {
         float v = ep.alpha * a;
-        if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, ok), v);
+        if (ep.beta != 0.0f) v = fmaf(ep.beta, cin, v);
         if constexpr (decltype(FUSED)::value) {
             if (ep.bias) v += bias;
             v = activate(ep.act, v);
         }
-        store_out(q, ok, v);
+        return v;
     };
     auto finish = [&](auto OUTK, auto FUSED) __attribute__((always_inline)) {
+        constexpr int ok = decltype(OUTK)::value;
         float bias[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             bias[j] = decltype(FUSED)::value && ep.bias && nb + 16 * j < p.N ? load_bias(ep, nb + 16 * j) : 0.0f;
+        // One 16-row block at a time: all of the block's C_in loads (beta != 0),
+        // then all of its values, then all of its stores.  A load or a use of a
+        // loaded value placed after a store would wait for that store too (the
+        // counter that tracks loads counts stores), and each element would pay
+        // a memory round trip; so would a load inside a per-element branch.
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            float cin[TN][4], out[TN][4];
+            if (ep.beta != 0.0f) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int n = nb + 16 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // clamped into the matrix: every lane loads (no branch
+                        // per element); values past the edge are never stored
+                        const int m = min(mb + 16 * i + e, p.M - 1), nc = min(n, p.N - 1);
+                        cin[j][e] = load_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)nc * ep.c_cs, ok);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    out[j][e] = value(FUSED, acc[i][j][e], bias[j], cin[j][e]);
+                    // pins the value here: the compiler would otherwise sink its
+                    // computation into the store's branch, after earlier stores
+                    asm volatile("" : "+v"(out[j][e]));
+                }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int n = nb + 16 * j;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = mb + 16 * i + e;
-                    if (m < p.M && n < p.N) store(OUTK, FUSED, m, n, acc[i][j][e], bias[j]);
+                    if (m < p.M && n < p.N) store_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs, ok, out[j][e]);
                 }
             }
+        }
     };
     auto finish_kind = [&](auto FUSED) __attribute__((always_inline)) {
         if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{}, FUSED);
@@ -514,34 +544,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     __syncthreads();
     if (!is_last) return;
     // The sum runs over s = 0..S-1 in order, this workgroup's own partial
-    // included; for each s all of the thread's elements are loaded together
-    // (one round trip per split, not one per split and element).
+    // included.  Loads go out in batches of QB splits x IB 16-row blocks (at
+    // most 64 values in flight beside the accumulators), every load of a batch
+    // before any add, so a batch costs one memory round trip; a batch running
+    // past the last split re-reads split S-1 (unconditional loads keep the
+    // waits exact) and ignores it.
     auto part = [&](int q, int i, int j, int e) __attribute__((always_inline)) {
         return __hip_atomic_load(slot(q, i, j, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = part(0, i, j, e);
-    // (IB 16-row blocks of a split at a time: at most 8 fragments of partials
-    // in registers beside the accumulators)
     constexpr int IB = TM < (8 / TN > 0 ? 8 / TN : 1) ? TM : (8 / TN > 0 ? 8 / TN : 1);
-    for (int q = 1; q < S; ++q) {
+    constexpr int QB = 16 / (IB * TN) > 0 ? 16 / (IB * TN) : 1;
 #pragma unroll
-        for (int i0 = 0; i0 < TM; i0 += IB) {
-            f32x4 v[IB][TN];
+    for (int i0 = 0; i0 < TM; i0 += IB) {
+        for (int q0 = 0; q0 < S; q0 += QB) {
+            f32x4 v[QB][IB][TN];
 #pragma unroll
-            for (int i = 0; i < IB; ++i)
+            for (int qq = 0; qq < QB; ++qq) {
+                const int q = min(q0 + qq, S - 1);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int i = 0; i < IB; ++i)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[i][j][e] = part(q, i0 + i, j, e);
+                    for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int i = 0; i < IB; ++i)
+                        for (int e = 0; e < 4; ++e) v[qq][i][j][e] = part(q, i0 + i, j, e);
+            }
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i0 + i][j] += v[i][j];
+            for (int qq = 0; qq < QB; ++qq) {
+                if (q0 + qq >= S) break;
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i0 + i][j] = q0 + qq == 0 ? v[qq][i][j] : acc[i0 + i][j] + v[qq][i][j];
+            }
         }
     }
     finish_any();
