@@ -229,31 +229,86 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[TM][TN], const Mfm
 #pragma unroll
     for (int j = 0; j < TN; ++j)
         bias[j] = FUSED && ep.bias && nb + 16 * j < p.N ? load_bias(ep, nb + 16 * j) : 0.0f;
+    // One 16 x 64 block at a time: all of its C_in loads (beta != 0, from
+    // addresses clamped into the matrix, so no per-element branch), then all of
+    // its values, then its stores.  A load, or a use of a loaded value, placed
+    // after a store would also wait for that store (one counter tracks both),
+    // and each element would pay a memory round trip.
+    if constexpr (TM * TN > 16) {
+        // The 256x256 tile's accumulators fill the registers: element by
+        // element (batching here spills the accumulators to scratch).
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = nb + 16 * j;
+            for (int j = 0; j < TN; ++j) {
+                const int n = nb + 16 * j;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = mb + 16 * i + e;
-                if (m < p.M && n < p.N) {
-                    const float a = acc[i][j][e];
-                    if (OUTK < 0) {
-                        p.ws[((int64_t)z * p.M + m) * p.N + n] = a;
-                    } else {
-                        char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
-                        float v = ep.alpha * a;
-                        if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, OUTK), v);
+                for (int e = 0; e < 4; ++e) {
+                    const int m = mb + 16 * i + e;
+                    if (m < p.M && n < p.N) {
+                        const float a = acc[i][j][e];
+                        if (OUTK < 0) {
+                            p.ws[((int64_t)z * p.M + m) * p.N + n] = a;
+                        } else {
+                            char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
+                            float v = ep.alpha * a;
+                            if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, OUTK), v);
+                            if (FUSED) {
+                                if (ep.bias) v += bias[j];
+                                v = activate(ep.act, v);
+                            }
+                            store_out(q, OUTK, v);
+                        }
+                    }
+                }
+            }
+        return;
+    }
+    constexpr int JB = TN < 4 ? TN : 4;   // 16-column blocks per batch (registers: 2 x 16 values)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j0 = 0; j0 < TN; j0 += JB) {
+            float out[JB][4];
+            if (OUTK >= 0) {
+                float cin[JB][4];
+                if (ep.beta != 0.0f) {
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = min(mb + 16 * i + e, p.M - 1), n = min(nb + 16 * (j0 + j), p.N - 1);
+                            cin[j][e] = load_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs, OUTK);
+                        }
+                }
+#pragma unroll
+                for (int j = 0; j < JB; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float v = ep.alpha * acc[i][j0 + j][e];
+                        if (ep.beta != 0.0f) v = fmaf(ep.beta, cin[j][e], v);
                         if (FUSED) {
-                            if (ep.bias) v += bias[j];
+                            if (ep.bias) v += bias[j0 + j];
                             v = activate(ep.act, v);
                         }
-                        store_out(q, OUTK, v);
+                        out[j][e] = v;
+                        asm volatile("" : "+v"(out[j][e]));   // computed here, not sunk past earlier stores
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                const int n = nb + 16 * (j0 + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = mb + 16 * i + e;
+                    if (m < p.M && n < p.N) {
+                        if (OUTK < 0) p.ws[((int64_t)z * p.M + m) * p.N + n] = acc[i][j0 + j][e];
+                        else store_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs, OUTK, out[j][e]);
                     }
                 }
             }
         }
+    }
 }
 
 // ------------------------------------------------------------------ the kernel
