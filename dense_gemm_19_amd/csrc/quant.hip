@@ -62,9 +62,17 @@ __device__ __forceinline__ float chunk_value(const Chunk<XT> &c, int j) {
     return XT == DG_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
 }
 
+// 32 zero bytes in device memory: the source of the vector loads of chunks
+// outside X (rows past M, or a tile past the last one).
+__device__ __attribute__((aligned(16))) const u32x4 g_qzero[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+
 // The thread's RT chunks of tile `tile`: rows r0 + 16 i of the tile's 16*RT rows,
-// columns 8 cc .. 8 cc + 7 of its 128; zeros outside X.
-template <int XT, int RT>
+// columns 8 cc .. 8 cc + 7 of its 128; zeros outside X.  VEC (X rows
+// K-contiguous with 16-byte aligned chunks, K a multiple of 8): one or two
+// 16-byte loads per chunk, every one issued (chunks outside X read the zero
+// block), with no branch, so the compiler's wait before the first use of a
+// tile counts exactly the loads issued after it.  Otherwise element loads.
+template <int XT, int RT, bool VEC>
 __device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, int cc, Chunk<XT> (&buf)[RT]) {
     const int mb = tile / p.tiles_k, kb = tile - mb * p.tiles_k;
     const int c0 = kb * 128 + cc * 8;
@@ -73,10 +81,12 @@ __device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, 
     for (int i = 0; i < RT; ++i) {
         const int row = mb * 16 * RT + r0 + 16 * i;
         const char *xr = p.X + (int64_t)row * p.x_rs;
-        if (row < p.M && nvalid == 8 && p.x_vec) {
+        if constexpr (VEC) {
+            const char *src = row < p.M && nvalid > 0 ? xr + (int64_t)c0 * (XT == DG_F32 ? 4 : 2)
+                                                      : reinterpret_cast<const char *>(g_qzero);
 #pragma unroll
             for (int h = 0; h < Chunk<XT>::W / 4; ++h) {
-                const u32x4 q = *reinterpret_cast<const u32x4 *>(xr + (int64_t)c0 * (XT == DG_F32 ? 4 : 2) + 16 * h);
+                const u32x4 q = *(const __attribute__((address_space(1))) u32x4 *)(src + 16 * h);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t w = q[j];   // (an element copied to a scalar before any bit cast)
@@ -166,19 +176,23 @@ __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, 
 // only).  Each workgroup walks tiles bid, bid + grid, ... with the next tile's
 // loads in flight while it quantizes and stores the current one, so that the
 // reads and writes of the whole grid overlap instead of running in two waves.
-template <int XT, int RT>
+template <int XT, int RT, bool VEC>
 __global__ void __launch_bounds__(256) quant_fp8(QuantArgs p, int ntiles) {
     __shared__ float wave_max[2][4];   // (double-buffered: the next tile writes the other half)
     const int t = threadIdx.x, cc = t & 15, r0 = t >> 4;
     Chunk<XT> b0[RT], b1[RT];
+    // The loads of a tile past the last one are issued too: its rows lie past M,
+    // so they read nothing and give zeros.  Unconditional loads keep the wait
+    // before each quantization exact (a load under a condition makes the
+    // compiler wait for every load in flight, the next tile's included).
     int tile = blockIdx.x;
-    if (tile < ntiles) load_tile<XT, RT>(p, tile, r0, cc, b0);
+    load_tile<XT, RT, VEC>(p, tile, r0, cc, b0);
     for (; tile < ntiles; tile += 2 * gridDim.x) {
         const int t1 = tile + gridDim.x, t2 = t1 + gridDim.x;
-        if (t1 < ntiles) load_tile<XT, RT>(p, t1, r0, cc, b1);
+        load_tile<XT, RT, VEC>(p, t1, r0, cc, b1);
         quant_tile<XT, RT>(p, tile, t, r0, cc, b0, wave_max[0]);
         if (t1 >= ntiles) break;
-        if (t2 < ntiles) load_tile<XT, RT>(p, t2, r0, cc, b0);
+        load_tile<XT, RT, VEC>(p, t2, r0, cc, b0);
         quant_tile<XT, RT>(p, t1, t, r0, cc, b1, wave_max[1]);
     }
 }
@@ -193,15 +207,22 @@ hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream, int
     const int64_t want = (int64_t)(cus > 0 ? cus : 256) * (a.block ? 3 : 4);
     const dim3 grid((unsigned)(ntiles < want ? ntiles : want)), block(256);
     const int n = (int)ntiles;
+    const bool vec = a.x_vec && a.K % 8 == 0;
+#define DG_QUANT_LAUNCH(XT, RT)                                                                       \
+    do {                                                                                              \
+        if (vec) hipLaunchKernelGGL((quant_fp8<XT, RT, true>), grid, block, 0, stream, a, n);        \
+        else hipLaunchKernelGGL((quant_fp8<XT, RT, false>), grid, block, 0, stream, a, n);           \
+    } while (0)
     if (a.block) {
-        if (x_dtype == DG_F32) hipLaunchKernelGGL((quant_fp8<DG_F32, 8>), grid, block, 0, stream, a, n);
-        else if (x_dtype == DG_F16) hipLaunchKernelGGL((quant_fp8<DG_F16, 8>), grid, block, 0, stream, a, n);
-        else hipLaunchKernelGGL((quant_fp8<DG_BF16, 8>), grid, block, 0, stream, a, n);
+        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 8);
+        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 8);
+        else DG_QUANT_LAUNCH(DG_BF16, 8);
     } else {
-        if (x_dtype == DG_F32) hipLaunchKernelGGL((quant_fp8<DG_F32, 4>), grid, block, 0, stream, a, n);
-        else if (x_dtype == DG_F16) hipLaunchKernelGGL((quant_fp8<DG_F16, 4>), grid, block, 0, stream, a, n);
-        else hipLaunchKernelGGL((quant_fp8<DG_BF16, 4>), grid, block, 0, stream, a, n);
+        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 4);
+        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 4);
+        else DG_QUANT_LAUNCH(DG_BF16, 4);
     }
+#undef DG_QUANT_LAUNCH
     return hipGetLastError();
 }
 
