@@ -4,13 +4,17 @@
                     [--no-cpu] [--copy-calib] [--no-calib]
 
 One step is one pass of the thin-GEMM workload the pages single out: the BF16
-x.W1 up-projection of an MoE FFN, [1,4096] x [4096,14336], followed by the
-query x 128-key cache product [1,4096] x [4096,128] (B = K_cache^T).  Both run
+x.W1 up-projection of an MoE FFN, [1,4096] x [4096,14336], and the query x
+128-key cache product [1,4096] x [4096,128] (B = K_cache^T).  Both run
 through the C ABI (view parse, plan, skinny streaming kernel, epilogue), with
 every input already resident in HBM: W1 and the cache are rotated over enough
 distinct copies (>= 1 GiB in all) that neither the 256 MB Infinity Cache nor
-the L2 can serve a repeat.  `value` is the step's algorithmic bytes (each
-operand read once, C written once) per second.
+the L2 can serve a repeat.  The two products are independent, so each runs on
+its own HIP stream (both at the default priority): the cache product's 128
+one-wave workgroups fill CUs that the x.W1 grid (224 workgroups) leaves free.
+`value` is the step's algorithmic bytes (each operand read once, C written
+once) per second over K steps; `one_stream` repeats the measurement with both
+products on one stream, one after the other.
 
 The JSON line also carries:
   roofline      the x.W1 kernel's achieved HBM rate (its algorithmic bytes over
@@ -137,9 +141,10 @@ class Call:
         return self.fn(*self.args)
 
 
-def prepared(dg, sets):
+def prepared(dg, sets, stream=None):
     import torch
-    stream = torch.cuda.current_stream().cuda_stream
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
     return [Call(dg, c, stream) for c in sets]
 
 
@@ -486,29 +491,51 @@ def main():
     log("plan x.W1:", dg.plan(sa_sets[0].A, sa_sets[0].B, sa_sets[0].C))
     log("plan q.Kc:", dg.plan(sb_sets[0].A, sb_sets[0].B, sb_sets[0].C))
 
-    calls_a, calls_b = prepared(dg, sa_sets), prepared(dg, sb_sets)
+    main_stream = torch.cuda.current_stream()
+    side_stream = torch.cuda.Stream()   # default priority, like every stream here
+    calls_a = prepared(dg, sa_sets)
+    calls_b = prepared(dg, sb_sets, side_stream.cuda_stream)
+    calls_b1 = prepared(dg, sb_sets)     # the same calls on the main stream
     na, nb = len(calls_a), len(calls_b)
 
-    def steps(lo, hi):
+    def steps(lo, hi, cb):
         bad = 0
         for i in range(lo, hi):
             bad |= calls_a[i % na]()
-            bad |= calls_b[i % nb]()
+            bad |= cb[i % nb]()
         if bad:
             raise RuntimeError("dg_gemm returned an error status in the timed loop")
 
-    steps(0, args.warmup)
+    def timed_steps(cb, two_streams):
+        # K whole steps between an event pair on the main stream; with two
+        # streams the side stream starts after the first event and the main
+        # stream waits for all of its work before the second
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(main_stream)
+        if two_streams:
+            side_stream.wait_event(t_start)
+        steps(args.warmup, args.warmup + args.steps, cb)
+        if two_streams:
+            joined = torch.cuda.Event()
+            joined.record(side_stream)
+            main_stream.wait_event(joined)
+        t_end.record(main_stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end)
+
+    steps(0, args.warmup, calls_b)
     torch.cuda.synchronize()
-    # timed region 1: K whole steps back to back on the current stream
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    steps(args.warmup, args.warmup + args.steps)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
+    # timed region 1: K whole steps, the two products on two streams
+    ms_total = timed_steps(calls_b, True)
     ms_step = ms_total / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # the same steps with both products on the main stream, one after the other
+    steps(0, args.warmup // 5, calls_b1)
+    torch.cuda.synchronize()
+    ms_total1 = timed_steps(calls_b1, False)
+    ms_step1 = ms_total1 / args.steps
+    value1 = step_bytes / (ms_step1 * 1e-3) / 1e9
     # timed region 2: the x.W1 launch alone, K launches back to back between a
     # HIP event pair on the stream the library launches on: the dominant
     # kernel's average launch duration
@@ -524,7 +551,8 @@ def main():
         raise RuntimeError("dg_gemm returned an error status")
     k_avg = k0.elapsed_time(k1) / args.steps
     achieved = bytes_a / (k_avg * 1e-3) / 1e9
-    log(f"{args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s; "
+    log(f"{args.steps} steps in {ms_total:.3f} ms: {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s "
+        f"(one stream: {ms_step1 * 1e3:.2f} us/step, {value1:.1f} GB/s); "
         f"x.W1 launch avg {k_avg * 1e3:.2f} us -> {achieved:.1f} GB/s")
     traffic = traffic_from_profiles(bytes_a)
     del sa_sets, sb_sets
@@ -575,7 +603,8 @@ def main():
                                "q[1,4096] . K_cache[128,4096]^T, FP32 accumulate, BF16 C",
                    "M": 1, "K": 4096, "N": [14336, 128], "buffer_sets": P,
                    "inputs": "N(0,1) seeded, resident in HBM, rotated over >= 1 GiB",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU; the two independent products on two HIP streams"},
+        "one_stream": {"value": round(value1, 1), "ms_per_step": round(ms_step1, 6)},
         "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": bytes_a,
