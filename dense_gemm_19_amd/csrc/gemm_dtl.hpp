@@ -253,9 +253,13 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
 // is a Stream-K-style hybrid: the pieces of the leftover tiles fill the last
 // wave of workgroup slots instead of leaving part of it idle (sheratonhq.com
 // deep dive, section 5.2, names Stream-K for balancing tails).
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
+    // Waves 0 .. NLD-1 issue the tile loads; NLD < NW leaves the others to
+    // matrix work alone (a wave stalls while it issues, the queue being full).
+    constexpr int NLD = NL > 0 ? NL : NW;
+    static_assert(NW % NLD == 0, "loader waves");
     constexpr int EB = InT<IN>::EB;
     constexpr bool F8 = (IN == IN_F8);
     constexpr int KSTEPS = F8 ? 1 : 2;          // 16-bit: matrix instructions of 32 K values
@@ -264,12 +268,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     constexpr int STAGE = SB_OFF + (F8 ? 256 : 0);
     constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 16, TN = WTN / 16;
     constexpr int KEL = KB / EB;
-    using AIO = DtlIO<AMODE, BM, EB, NW>;
-    using BIO = DtlIO<BMODE, BN, EB, NW>;
+    using AIO = DtlIO<AMODE, BM, EB, NLD>;
+    using BIO = DtlIO<BMODE, BN, EB, NLD>;
     constexpr int PER_FILL = AIO::INSTS + BIO::INSTS + (F8 ? 2 : 0);   // loads per wave per tile
     static_assert(NS >= 2 && NS <= 8, "2..8 stages");
     static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns lie in one 128-column scale block");
     static_assert(BM % 64 == 0 || !F8, "row scales are staged 64 per wave");
+    static_assert(!F8 || NLD >= BM / 64, "row scales are staged by the loader waves");
     static_assert((NS - 2) * PER_FILL <= 63, "vmcnt range");
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
@@ -308,8 +313,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     // Source addresses are computed once; each tile only adds a uniform K offset.
     // The LDS destinations are uniform too (the wave index, made uniform once).
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const typename AIO::Src a_src = AIO::sources(p.a, m0, p.M, wave, lane);
-    const typename BIO::Src b_src = BIO::sources(p.b, n0, p.N, wave, lane);
+    const typename AIO::Src a_src = AIO::sources(p.a, m0, p.M, wave % NLD, lane);
+    const typename BIO::Src b_src = BIO::sources(p.b, n0, p.N, wave % NLD, lane);
     const uint32_t sa_off = F8 ? (uint32_t)((int64_t)sa_row * p.sa_rs) : 0u;
     const uint32_t sb_off = F8 ? (uint32_t)((int64_t)sb_blk * p.sb_cs) : 0u;
     const char *a_org = p.a.ptr + (int64_t)m0 * p.a.r_stride;
@@ -318,6 +323,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     const uint32_t ring_lds = lds_addr(ring);
 
     auto fill = [&](int stage_idx, int kt) __attribute__((always_inline)) {   // K tile kt into a stage
+        if (NLD < NW && wave_u >= NLD) return;
         const uint32_t st = ring_lds + (uint32_t)(stage_idx * STAGE);
         AIO::issue(st, a_src, a_org + kt * a_kstep, wave_u);
         BIO::issue(st + A_BYTES, b_src, b_org + kt * b_kstep, wave_u);
@@ -583,7 +589,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL>
 hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
     const int tiles = a.tiles_m * a.tiles_n;
@@ -591,26 +597,29 @@ hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
     if (a.splits > 1) {
         grid = dim3(a.dp_tiles + (tiles - a.dp_tiles) * a.splits);
         if constexpr (TM * TN <= 16) {
-            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true>), grid, dim3(64 * WGM * WGN), 0, s, a);
+            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true, NL>), grid, dim3(64 * WGM * WGN), 0, s, a);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;   // no split K for this tile (the planner never asks)
         }
     }
-    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false>), grid, dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, NL>), grid, dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int NL = 0>
 hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
-    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ>(a, s);
-    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ>(a, s);
-    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ>(a, s);
-    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ>(a, s);
+    if (am == KMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ, NL>(a, s);
+    if (am == KMAJ && bm == MNMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ, NL>(a, s);
+    if (am == MNMAJ && bm == KMAJ) return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ, NL>(a, s);
+    return launch_t<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ, NL>(a, s);
 }
 
 // Tile configurations (see kernels.hpp): 256x256 runs 8 waves of 128x64 with 2
-// stages (one workgroup per CU); 128x128 4 waves of 64x64 with 2 stages (two
+// stages (one workgroup per CU), of which waves 0-3 (one per SIMD) issue all
+// the tile loads and waves 4-7 only compute: a wave stalls while it issues
+// (the memory queue is full), and this way every SIMD keeps a wave on the
+// matrix cores meanwhile (BF16 4096^3: 115 -> 109 us); 128x128 4 waves of 64x64 with 2 stages (two
 // workgroups share a CU, so that one's loads overlap the other's matrix
 // work); the small tiles, used for HBM-bound shapes with few rows, 4 waves
 // with deep rings (6 or 8 stages), so that enough bytes stream per CU to cover
@@ -619,7 +628,7 @@ hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
 template <int IN>
 hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
     switch (tile) {
-    case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2>(am, bm, a, s);
+    case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2, 4>(am, bm, a, s);
     case T128x128: return launch_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, s);
     case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
     case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);
