@@ -170,13 +170,19 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
             tile = p.fp8 ? T64x128 : T64x64;
             if (p.M > 64 && !p.fp8 && tile_eff(p.M, p.N, T128x64) > tile_eff(p.M, p.N, tile) + 1e-9) tile = T128x64;
         } else {
-            // Enough rows for a compute-bound shape: the largest tile (FP8 stops at
-            // 128x128, whose promotion fits the registers) that still gives every
-            // CU a tile, else the one giving the most tiles.
+            // Enough rows for a compute-bound shape: the largest tile that still
+            // gives every CU a tile, else the one giving the most tiles.  FP8 takes
+            // 256x256 (one workgroup per CU, no K split) only where its tiles fill
+            // at least 3/4 of the CU waves they occupy; a short last wave is
+            // better served by 128x128 and its split tail.  Measured on
+            // 4096x7168x4096: 256x256 148.9 us, 128x128 171 us.
             const int order[] = {T256x256, T128x128, T128x64, T64x64};
             int64_t best_tiles = -1;
             for (int t : order) {
-                if (p.fp8 && t == T256x256) continue;
+                if (p.fp8 && t == T256x256) {
+                    const int64_t nt = tile_count(p.M, p.N, t);
+                    if (nt < d.cus || (double)nt / (double)(cdiv(nt, d.cus) * d.cus) < 0.75) continue;
+                }
                 if (tile_eff(p.M, p.N, t) < 0.75 && t != T64x64) continue;
                 const int64_t nt = tile_count(p.M, p.N, t);
                 if (nt >= d.cus) { tile = t; break; }
@@ -184,7 +190,7 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
             }
         }
         if (overrides().force_tile >= 0) tile = overrides().force_tile;
-        if (c.tile >= 0 && !(p.fp8 && c.tile == T256x256)) tile = c.tile;
+        if (c.tile >= 0) tile = c.tile;
     } else if (!pl.slow) {
         // general kernel (register-staged loads, K tails): tiles it implements
         const int order[] = {T256x256, T128x128, T128x64, T64x64};
@@ -465,7 +471,7 @@ std::vector<PlanChoice> candidate_choices(const Problem &p, const Device &d) {
         else if (!def.slow) tiles = {T256x256, T128x128, T128x64, T64x64};
         else tiles = {-1};
         for (int t : tiles) {
-            if (t >= 0 && p.fp8 && t == T256x256) continue;
+            if (t >= 0 && p.fp8 && t == T256x256 && !def.dtl) continue;   // (the register-staged kernel spills)
             // no tile larger than the matrix in either dimension
             if (t >= 0 && (mfma_tile_bm(t) > std::max<int64_t>(64, p.M) || mfma_tile_bn(t) > std::max<int64_t>(64, p.N)))
                 continue;

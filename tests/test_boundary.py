@@ -205,6 +205,23 @@ def test_plans_for_the_workloads():
     assert field(p, "path") == "scale"
 
 
+def test_fp8_tile_choice():
+    """FP8 takes the 256x256 tile where its tiles fill at least 3/4 of the CU waves,
+    else 128x128 (with the split tail where the last wave is short)."""
+    E4 = torch.float8_e4m3fn
+
+    def fp8_plan(M, N, K):
+        sa, sb = torch.ones(M, -(-K // 128)), torch.ones(-(-K // 128), -(-N // 128))
+        return dg.plan(torch.empty(M, K, dtype=E4), torch.empty(K, N, dtype=E4),
+                       torch.empty(M, N, dtype=torch.bfloat16), 1.0, 0.0, sa, sb)
+    p = fp8_plan(4096, 7168, 4096)     # 448 tiles over 256 CUs: 7/8 of two waves
+    assert field(p, "tile") == "256x256" and field(p, "splits") == "1", p
+    p = fp8_plan(4096, 4224, 4096)     # 272 tiles: the second wave would hold 16
+    assert field(p, "tile") == "128x128" and int(field(p, "dp_tiles")) > 0, p
+    p = fp8_plan(2048, 2048, 2048)     # 64 tiles of 256x256: too few
+    assert field(p, "tile") == "128x128", p
+
+
 def test_calib_argument_errors():
     """The calibration entry points reject bad arguments before touching a device."""
     import ctypes

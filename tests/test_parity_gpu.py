@@ -135,6 +135,22 @@ def test_integer_inputs_bitwise(dg, kind):
     check(dg, cb, expect_bitwise=True)
 
 
+def test_fp8_256x256_integer_bitwise(dg):
+    # The FP8 256x256 tile (loader waves, promotion in registers): integer-valued
+    # codes with power-of-two scales give exact sums, so the output is bitwise
+    # the oracle's on every sampled row.
+    g = synth.rng(79)
+    M, N, K = 4096, 4096, 512
+    A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), torch.float32).to(E4M3)
+    B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), torch.float32).to(E4M3)
+    sa = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(M, K // 128)))).float()
+    sb = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(K // 128, N // 128)))).float()
+    c = synth.Case("int_fp8_256", A, B, torch.zeros(M, N), 1.0, 0.0, sa, sb, rtol=1e-3)
+    tile, text = _plan_field(dg, c, "tile")
+    assert tile == "256x256", text
+    check(dg, c, rows=_sample_rows(M, seed=79), expect_bitwise=True)
+
+
 def test_run_twice_bitwise(dg):
     for case in [synth.gemm_case(64, 512, 2048, F16, torch.float32, seed=1),      # split-K
                  synth.gemm_case(1, 4096, 4096, BF16, BF16, seed=2),              # skinny
