@@ -51,13 +51,16 @@ __device__ __forceinline__ int kmaj_off(int r, int c) { return r * KB + ((c ^ (r
 // transpose reads of one 16-lane group touch 4 (16-bit) or 8 (8-bit) consecutive
 // K rows; the swizzle spreads those rows, and the K rows of the lane group read
 // in the same LDS cycle (K bits 3-4 for 16-bit; for 8-bit, bit 4, which tells
-// lane groups 0/1 and 2/3 of a read apart), over distinct banks.
+// lane groups 0/1 and 2/3 of a read apart), over distinct banks.  8-bit rows of
+// 256 bytes (16 chunks) all start on bank 0: chunk (k & 7) ^ 8 * (bit 4 of k)
+// gives lane groups 0 and 1 (and 2 and 3), which read together, the two halves
+// of the banks.
 template <int EB, int CPR>
 __device__ __forceinline__ int mn_swz(int k) {
     int s;
     if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
     else if (CPR >= 32) s = (k & 7) | (((k >> 5) & 3) << 3);
-    else if (CPR >= 16) s = (k & 7) ^ ((k >> 5) & 3) ^ (((k >> 5) & 1) << 3);
+    else if (CPR >= 16) s = (k & 7) ^ (((k >> 4) & 1) << 3);
     else s = (k & 7) ^ ((k >> 4) & 1);
     return s & (CPR - 1);
 }
