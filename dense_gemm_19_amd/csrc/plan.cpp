@@ -212,8 +212,14 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
     int64_t S = 1;
     const int64_t nt = tile_count(p.M, p.N, tile);
     if (pl.dtl) {
-        if (p.M <= 128) S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 16));
-        else if (nt < d.cus && tile != T256x256 && tile != T128x128)
+        if (p.M <= 128) {
+            S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 16));
+            // Very few tiles (a quarter of the CUs or less): up to 4 splits of as
+            // few as 2 K tiles; the split-K sum loads its partials in one round
+            // trip, so short splits pay (FP16 64x512x512: 6.9 -> 6.4 us with 4).
+            if (nt * 4 <= d.cus)
+                S = std::max<int64_t>(S, std::min<int64_t>({cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2), 4}));
+        } else if (nt < d.cus && tile != T256x256 && tile != T128x128)
             S = std::max<int64_t>(1, std::min<int64_t>(cdiv(d.cus, nt), pl.ktiles / 8));
     } else if (!pl.slow) {
         if (nt < d.cus) S = std::min<int64_t>(cdiv(d.cus, nt), std::max<int64_t>(1, pl.ktiles / 2));
