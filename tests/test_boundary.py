@@ -205,6 +205,18 @@ def test_plans_for_the_workloads():
     assert field(p, "path") == "scale"
 
 
+def test_few_tile_k_split():
+    """Few-row problems with very few tiles split K into up to 4 pieces of at
+    least 2 K tiles; larger ones keep at least 16 K tiles per piece."""
+    t = lambda *s, dt=torch.half: torch.empty(*s, dtype=dt)
+    p = dg.plan(t(64, 512), t(512, 512), t(64, 512, dt=torch.float32))        # 8 tiles, 8 K tiles
+    assert field(p, "tile") == "64x64" and field(p, "splits") == "4", p
+    p = dg.plan(t(64, 4096), t(4096, 4096), t(64, 4096, dt=torch.float32))    # 64 tiles, 64 K tiles
+    assert field(p, "splits") == "4", p
+    p = dg.plan(t(16, 64), t(64, 256), t(16, 256, dt=torch.float32))          # 1 K tile: nothing to split
+    assert field(p, "splits") == "1", p
+
+
 def test_fp8_tile_choice():
     """FP8 takes the 256x256 tile where its tiles fill at least 3/4 of the CU waves,
     else 128x128 (with the split tail where the last wave is short)."""
