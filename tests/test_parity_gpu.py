@@ -265,6 +265,35 @@ def test_dtl_tiles(dg, kind, layouts, shape):
     check(dg, c, rows=_sample_rows(M, seed=seed))
 
 
+@pytest.mark.parametrize("out", [BF16, torch.float32, F16], ids=["bf16", "f32", "f16"])
+def test_dtl_256_row_stores(dg, out):
+    # The 256x256 tile's epilogue: an M edge that cuts a tile, an N edge,
+    # beta != 0 (C_in read), every output type.
+    M, N, K = 4000, 4360, 256
+    c = synth.gemm_case(M, N, K, F16 if out == F16 else BF16, out, seed=811 + out.itemsize,
+                        alpha=1.25, beta=0.5)
+    tile, text = _plan_field(dg, c, "tile")
+    assert tile == "256x256", text
+    check(dg, c, rows=_sample_rows(M, seed=81))
+
+
+def test_dtl_256_row_stores_misaligned_window(dg):
+    # C is a window at column offset 1 of a wider buffer (no row is 8-byte
+    # aligned): every element lands in the window, nothing outside it is touched.
+    M, N, K = 4096, 4096, 256
+    big = torch.full((M + 2, N + 8), 777.0, dtype=BF16)
+    Cwin = big[1:1 + M, 1:1 + N]
+    c0 = synth.gemm_case(M, N, K, BF16, BF16, seed=812)
+    c = synth.Case("win256", c0.A, c0.B, Cwin, 1.0, 0.0)
+    tile, text = _plan_field(dg, c, "tile")
+    assert tile == "256x256", text
+    rep, d = check(dg, c, rows=_sample_rows(M, seed=82))
+    full = torch.empty(0, dtype=BF16, device=DEV).set_(d.C.untyped_storage()).view(M + 2, N + 8).cpu()
+    mask = torch.ones_like(full, dtype=torch.bool)
+    mask[1:1 + M, 1:1 + N] = False
+    assert (full[mask] == 777.0).all()
+
+
 # ---------------------------------------------------------------- the split tail of the last wave
 
 TAIL_CASES = [
