@@ -347,31 +347,32 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             for (int j = 0; j < TN; ++j) fb[j] = frag8<BMODE, BN>(lb, wn * WTN + 16 * j, lane);
             // Block sums over this 128-wide K block on the matrix cores, then
             // promotion into the FP32 accumulators with the scales applied once.
-            // The promotion of block t runs after the matrix instruction of block
-            // t + 1 is issued, so the vector ALUs work while the matrix core does.
+            // The promotion of block t runs after the matrix instructions of blocks
+            // t + 1 and t + 2 are issued, so the vector ALUs work while the matrix
+            // core does.
+            constexpr int PL = 2;   // promotion lag, in blocks
             i32x8 fa;
-            f32x4 s4[TM], prev;
+            f32x4 s4[TM], blk[TM * TN];
 #pragma unroll
-            for (int t = 0; t < TM * TN; ++t) {
-                const int i = t / TN, j = t % TN;
-                if (j == 0) {
-                    fa = frag8<AMODE, BM>(la, wm * WTM + 16 * i, lane);
-                    const f32x4 sa4 = *reinterpret_cast<const f32x4 *>(lsa + wm * WTM + 16 * i + 4 * (lane >> 4));
-                    s4[i] = sa4 * sb;
+            for (int t = 0; t < TM * TN + PL; ++t) {
+                if (t < TM * TN) {
+                    const int i = t / TN, j = t % TN;
+                    if (j == 0) {
+                        fa = frag8<AMODE, BM>(la, wm * WTM + 16 * i, lane);
+                        const f32x4 sa4 = *reinterpret_cast<const f32x4 *>(lsa + wm * WTM + 16 * i + 4 * (lane >> 4));
+                        s4[i] = sa4 * sb;
+                    }
+                    blk[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fa, fb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
-                const f32x4 blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fa, fb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (t > 0) {
-                    const int pi = (t - 1) / TN, pj = (t - 1) % TN;
+                if (t >= PL) {
+                    const int u = t - PL, pi = u / TN, pj = u % TN;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(s4[pi][e], prev[e], acc[pi][pj][e]);
+                    for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(s4[pi][e], blk[u][e], acc[pi][pj][e]);
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
-                prev = blk;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[TM - 1][TN - 1][e] = fmaf(s4[TM - 1][e], prev[e], acc[TM - 1][TN - 1][e]);
         } else {
             // The wave's B fragments of a K step stay in registers; A fragments
             // are read one 16-row block at a time, PD blocks ahead of the matrix
