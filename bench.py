@@ -478,7 +478,7 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
 
-    # ---- the step: x.W1 then q.K_cache^T, rotated over >= 1 GiB of distinct buffers
+    # ---- the step: x.W1 and q.K_cache^T (each on its own stream), rotated over >= 1 GiB of distinct buffers
     c2a, c2b = synth.config("c2a"), synth.config("c2b")
     sa_sets = rotated_sets(c2a, dev)
     sb_sets = rotated_sets(c2b, dev)
