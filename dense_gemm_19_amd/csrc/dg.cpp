@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -140,63 +141,95 @@ dg_status current_device(Device *d, bool require) {
     return DG_SUCCESS;
 }
 
-// Split-K scratch: per (device, stream), an FP32 partial-sum buffer and a block
-// of arrival counters, grown on demand and kept for the life of the process.
-// Work on one stream runs in order, so a stream's buffers are never used by two
-// launches at once; different streams never share them.  Counters are zeroed
-// (on the stream) when allocated, and every kernel that uses them leaves them
-// at zero.  Growing waits for the stream, since the old buffer may be in use.
-struct Workspace {
+// Split-K scratch: per (device, stream), one block of FP32 partial sums and one
+// of arrival counters, allocated in stream order on that stream (sheratonhq.com
+// deep dive, section 5.2: split-K partials in a workspace; kwkr.cn article,
+// troubleshooting table in 5.1: state shared by host threads must be
+// thread-safe).
+//  - A call leases its stream's entry: the entry's lock is held from the lookup
+//    until the call has enqueued every kernel that uses the blocks, so another
+//    host thread on the same stream can neither grow them nor launch on them in
+//    between.  Work on one stream runs in order, so successive calls reuse the
+//    blocks safely; different streams never share them.
+//  - Growing enqueues hipMallocAsync of the larger block and then hipFreeAsync
+//    of the old one, both on the stream: the old block is released after every
+//    launch already enqueued there, and the host never waits.
+//  - New counters are zeroed by a kernel on the stream; every kernel that uses
+//    them leaves them at zero.
+//  - Entries are never evicted: a (device, stream) that ran a split-K GEMM keeps
+//    its blocks until the process ends.
+struct WsEntry {
+    int dev = 0;
+    hipStream_t stream = nullptr;
     std::mutex mu;
-    struct Entry { int dev; hipStream_t stream; void *ptr; size_t bytes; int *cnt; size_t ncnt; };
-    Entry e[64];
-    int n = 0;
+    float *ws = nullptr;
+    size_t bytes = 0;
+    int *cnt = nullptr;
+    size_t ncnt = 0;
 };
 
-Workspace &workspace() {
-    static Workspace w;
-    return w;
+struct WsTable {
+    std::mutex mu;
+    std::vector<std::unique_ptr<WsEntry>> entries;
+};
+
+WsTable &ws_table() {
+    static WsTable t;
+    return t;
 }
 
-hipError_t release(Workspace::Entry &x) {
-    hipError_t err = hipSuccess;
-    if (x.ptr || x.cnt) err = hipStreamSynchronize(x.stream);
-    if (err == hipSuccess && x.ptr) err = hipFree(x.ptr);
-    if (err == hipSuccess && x.cnt) err = hipFree(x.cnt);
-    x.ptr = nullptr; x.bytes = 0; x.cnt = nullptr; x.ncnt = 0;
-    return err;
-}
+// The blocks of one call (null when the plan needs none), locked while it lives.
+struct WsLease {
+    std::unique_lock<std::mutex> lock;
+    float *ws = nullptr;
+    int *counters = nullptr;
+};
 
-hipError_t get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, float **ws, int **counters) {
+hipError_t lease_workspace(hipStream_t stream, size_t bytes, size_t ncounters, WsLease *out) {
+    if (bytes == 0 && ncounters == 0) return hipSuccess;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    Workspace &w = workspace();
-    std::lock_guard<std::mutex> g(w.mu);
-    Workspace::Entry *slot = nullptr;
-    for (int i = 0; i < w.n; ++i)
-        if (w.e[i].dev == dev && w.e[i].stream == stream) slot = &w.e[i];
-    if (!slot) {
-        if (w.n == 64) {   // table full: recycle the oldest entry after its stream drains
-            if ((err = release(w.e[0])) != hipSuccess) return err;
-            for (int i = 1; i < w.n; ++i) w.e[i - 1] = w.e[i];
-            --w.n;
+    WsEntry *e = nullptr;
+    {
+        WsTable &t = ws_table();
+        std::lock_guard<std::mutex> g(t.mu);
+        for (auto &x : t.entries)
+            if (x->dev == dev && x->stream == stream) e = x.get();
+        if (!e) {
+            t.entries.push_back(std::make_unique<WsEntry>());
+            e = t.entries.back().get();
+            e->dev = dev;
+            e->stream = stream;
         }
-        slot = &w.e[w.n++];
-        *slot = Workspace::Entry{dev, stream, nullptr, 0, nullptr, 0};
     }
-    if (slot->bytes < bytes || slot->ncnt < ncounters) {
-        const size_t want_b = std::max<size_t>({bytes, slot->bytes, 1 << 20});
-        const size_t want_c = std::max<size_t>({ncounters, slot->ncnt, 4096});
-        if ((err = release(*slot)) != hipSuccess) return err;
-        if ((err = hipMalloc(&slot->ptr, want_b)) != hipSuccess) return err;
-        slot->bytes = want_b;
-        if ((err = hipMalloc(reinterpret_cast<void **>(&slot->cnt), want_c * sizeof(int))) != hipSuccess) return err;
-        slot->ncnt = want_c;
-        if ((err = hipMemsetAsync(slot->cnt, 0, want_c * sizeof(int), stream)) != hipSuccess) return err;
+    std::unique_lock<std::mutex> lk(e->mu);
+    if (e->bytes < bytes) {
+        const size_t want = std::max<size_t>({bytes, 2 * e->bytes, (size_t)1 << 20});
+        void *p = nullptr;
+        if ((err = hipMallocAsync(&p, want, stream)) != hipSuccess) return err;
+        if (e->ws && (err = hipFreeAsync(e->ws, stream)) != hipSuccess) {
+            (void)hipFreeAsync(p, stream);
+            return err;
+        }
+        e->ws = static_cast<float *>(p);
+        e->bytes = want;
     }
-    *ws = static_cast<float *>(slot->ptr);
-    *counters = slot->cnt;
+    if (e->ncnt < ncounters) {
+        const size_t want = std::max<size_t>({ncounters, 2 * e->ncnt, (size_t)4096});
+        void *p = nullptr;
+        if ((err = hipMallocAsync(&p, want * sizeof(int), stream)) != hipSuccess) return err;
+        if ((err = launch_fill_zero(static_cast<int *>(p), (int64_t)want, stream)) != hipSuccess) {
+            (void)hipFreeAsync(p, stream);
+            return err;
+        }
+        if (e->cnt && (err = hipFreeAsync(e->cnt, stream)) != hipSuccess) return err;
+        e->cnt = static_cast<int *>(p);
+        e->ncnt = want;
+    }
+    out->ws = e->ws;
+    out->counters = e->cnt;
+    out->lock = std::move(lk);
     return hipSuccess;
 }
 
@@ -226,19 +259,23 @@ Epilogue make_epi(const Problem &p) {
     return e;
 }
 
-dg_status run_plan(const Problem &p, const Plan &pl, hipStream_t stream) {
+// Device scratch of one call: split-K partials (pl.ws_bytes) and arrival
+// counters (pl.counters, zero on entry), or null when the plan needs none.
+struct Scratch {
+    float *ws = nullptr;
+    int *counters = nullptr;
+};
+
+// Enqueue the kernels of a plan whose scratch the caller provides.
+dg_status launch_plan(const Problem &p, const Plan &pl, const Scratch &sc, hipStream_t stream) {
     const Epilogue epi = make_epi(p);
     if (pl.path == Path::Noop) return DG_SUCCESS;
     if (pl.path == Path::Scale) {
         ScaleArgs s{epi, (int)p.M, (int)p.N};
         return launch_scale(s, stream) == hipSuccess ? DG_SUCCESS : DG_ERR_HIP;
     }
-    float *ws = nullptr;
-    int *counters = nullptr;
-    if (pl.splits > 1 && get_workspace(stream, pl.ws_bytes, (size_t)pl.counters, &ws, &counters) != hipSuccess) {
-        (void)hipGetLastError();
-        return DG_ERR_HIP;
-    }
+    float *ws = sc.ws;
+    int *counters = sc.counters;
     hipError_t e;
     if (pl.path == Path::Skinny) {
         SkinnyArgs a;
@@ -290,6 +327,17 @@ dg_status run_plan(const Problem &p, const Plan &pl, hipStream_t stream) {
         if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return DG_ERR_HIP;
     }
     return DG_SUCCESS;
+}
+
+// Enqueue a plan on the stream's own split-K workspace (leased until the
+// kernels are enqueued).
+dg_status run_plan(const Problem &p, const Plan &pl, hipStream_t stream) {
+    WsLease lease;
+    if (pl.splits > 1 && lease_workspace(stream, pl.ws_bytes, (size_t)pl.counters, &lease) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return launch_plan(p, pl, Scratch{lease.ws, lease.counters}, stream);
 }
 
 dg_status run(const Problem &p, const Device &d, hipStream_t stream) {
@@ -442,14 +490,30 @@ dg_status grouped_entry(int G, const dg_view *A, const dg_view *B, const dg_view
                 if (!m->empty() && (st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
     }
     const GroupedPlan gp = plan_grouped(ps, d);
+    // One workspace lease for every launch of the call, sized for the largest
+    // of them (the launches run in order on the stream, so they share it), taken
+    // before anything is enqueued.
+    size_t ws_bytes = 0, ncounters = 0;
     for (const GroupBatch &b : gp.batches) {
-        float *ws = nullptr;
-        int *counters = nullptr;
-        if (b.ws_floats > 0 &&
-            get_workspace(stream, b.ws_floats * sizeof(float), b.counters, &ws, &counters) != hipSuccess) {
-            (void)hipGetLastError();
-            return DG_ERR_HIP;
+        ws_bytes = std::max(ws_bytes, b.ws_floats * sizeof(float));
+        ncounters = std::max(ncounters, b.counters);
+    }
+    std::vector<Plan> solo_plans;
+    for (int g : gp.solo) {
+        solo_plans.push_back(cached_plan(ps[g], d));
+        if (solo_plans.back().splits > 1) {
+            ws_bytes = std::max(ws_bytes, solo_plans.back().ws_bytes);
+            ncounters = std::max(ncounters, (size_t)solo_plans.back().counters);
         }
+    }
+    WsLease lease;
+    if (lease_workspace(stream, ws_bytes, ncounters, &lease) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    for (const GroupBatch &b : gp.batches) {
+        float *ws = lease.ws;
+        int *counters = lease.counters;
         GroupedSkinnyArgs ga;
         std::memset(&ga, 0, sizeof ga);
         ga.ngroups = (int)b.groups.size();
@@ -484,8 +548,10 @@ dg_status grouped_entry(int G, const dg_view *A, const dg_view *B, const dg_view
             return DG_ERR_HIP;
         }
     }
-    for (int g : gp.solo)
-        if ((st = run(ps[g], d, stream)) != DG_SUCCESS) return st;
+    for (size_t i = 0; i < gp.solo.size(); ++i)
+        if ((st = launch_plan(ps[gp.solo[i]], solo_plans[i], Scratch{lease.ws, lease.counters}, stream)) !=
+            DG_SUCCESS)
+            return st;
     if (env_on("DG_SYNC_DEBUG")) {
         if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return DG_ERR_HIP;
     }

@@ -35,6 +35,12 @@ __global__ void __launch_bounds__(NT) scale_c(ScaleArgs p) {
     }
 }
 
+// n ints <- 0: the split-K arrival counters of a new workspace block (a kernel,
+// not hipMemsetAsync, so that a caller may capture the call in a HIP graph).
+__global__ void __launch_bounds__(NT) fill_zero(int *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) p[i] = 0;
+}
+
 int blocks_for(int64_t total) {
     int64_t b = (total + NT - 1) / NT;
     if (b > 65536) b = 65536;
@@ -42,6 +48,12 @@ int blocks_for(int64_t total) {
 }
 
 }  // namespace
+
+hipError_t launch_fill_zero(int *p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero, dim3(blocks_for(n)), dim3(NT), 0, stream, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream) {
     hipLaunchKernelGGL(splitk_reduce, dim3(blocks_for((int64_t)args.M * args.N)), dim3(NT), 0, stream, args);

@@ -77,7 +77,7 @@ struct SkinnyArgs {
     int *counters;                        // SK_BN, S > 1: one per column slab, 0 on entry and exit
     int M, N, K;
     int in_kind;                          // IN_F16 / IN_BF16
-    int a_vec;                            // SK_BK: A rows K-contiguous and 16-byte aligned
+    int a_vec;                            // A rows K-contiguous and 16-byte aligned (SK_BN: and K % 8 == 0)
     int splits;                           // S
     int k_per_split;                      // rows of K per split (multiple of 8)
     int kc;                               // SK_BN: rows of A staged in LDS at a time
@@ -155,5 +155,7 @@ hipError_t launch_skinny_grouped(int in_kind, int m_max, const GroupedSkinnyArgs
                                  int lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);
+hipError_t launch_fill_zero(int *p, int64_t n, hipStream_t stream);
+
 
 }  // namespace dg

@@ -39,10 +39,18 @@
  *    during execution surface at the caller's next synchronization.
  *  - On any error return, C has not been touched and nothing was enqueued.
  *  - Thread safety: every entry point may be called concurrently from several
- *    host threads and on several streams.  Split-K scratch memory is a
- *    library-owned device buffer per (device, stream), allocated with hipMalloc
- *    on first need, grown on demand (after waiting for that stream) and kept
- *    until the process ends; calls on different streams never share one.
+ *    host threads and on several streams.  Split-K scratch memory (partial
+ *    sums and arrival counters) is library-owned device memory per (device,
+ *    stream), allocated in stream order on that stream (hipMallocAsync) on
+ *    first need.  When a call needs more, the larger block is allocated and
+ *    the old one released with hipFreeAsync, both on the stream, so the old
+ *    block is freed only after the work already enqueued there; the host never
+ *    waits.  A call holds its stream's scratch from lookup until its kernels
+ *    are enqueued, so two host threads may share one stream.  Calls on
+ *    different streams never share scratch.  Scratch is kept until the process
+ *    ends.  (kwkr.cn article, troubleshooting table in section 5.1: state that
+ *    host threads share must be thread-safe; sheratonhq.com deep dive, section
+ *    5.2: split-K partials in a workspace.)
  */
 #ifndef DG_H
 #define DG_H
@@ -279,7 +287,11 @@ int32_t dg_tune_count(void);
  * Validate the arguments of dg_gemm exactly as dg_gemm does and write a
  * one-line, NUL-terminated description of the chosen plan (path, tiles,
  * split-K, grid, canonical operand layouts) into buf[0..len-1], without
- * launching anything.  Needs no GPU: with no device visible it plans for a
+ * launching anything.  The pages check a problem against its views before any
+ * kernel runs (a K disagreement is an error when the kernel is specialized,
+ * not an assertion at run time) and pick the kernel variant per shape and
+ * dtype from a cache (kwkr.cn article, sections 4.2 and 6.1); this call
+ * exposes that step on its own.  Needs no GPU: with no device visible it plans for a
  * 256-CU gfx950.  Returns the status dg_gemm would return before launching.
  * buf may be NULL only if len == 0.  A tuned plan (dg_gemm_tune,
  * dg_tune_load) of the same key is the one described.
@@ -287,12 +299,13 @@ int32_t dg_tune_count(void);
 dg_status dg_gemm_plan(const dg_view *A, const dg_view *B, const dg_view *C,
                        float alpha, float beta, char *buf, size_t len);
 
-/* Same as dg_gemm_plan for the arguments of dg_gemm_fp8. */
+/* Same as dg_gemm_plan for the arguments of dg_gemm_fp8 (kwkr.cn article,
+ * sections 4.2 and 6.1; the FP8 operands and scales of sheratonhq.com deep
+ * dive, section 2.4). */
 dg_status dg_gemm_fp8_plan(const dg_view *A, const dg_view *A_scale, const dg_view *B,
                            const dg_view *B_scale, const dg_view *C, float alpha, float beta,
                            char *buf, size_t len);
 
-/* Static, human-readable name of a status code ("DG_ERR_ALIAS", ...). */
 /*
  * FP8 E4M3 quantization of X, the producer of dg_gemm_fp8's operands: FP8 GEMM
  * needs per-token or per-block FP32 scale factors that squeeze each block into
@@ -323,9 +336,11 @@ typedef enum { DG_QUANT_TOKEN = 0, DG_QUANT_BLOCK = 1 } dg_quant_mode;
 dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_quant_mode mode,
                        hipStream_t stream);
 
+/* Helper (no page passage): static, human-readable name of a status code
+ * ("DG_ERR_ALIAS", ...); "DG_ERR_UNKNOWN" for a value outside dg_status. */
 const char *dg_status_str(dg_status s);
 
-/* DG_VERSION of the built library. */
+/* Helper (no page passage): DG_VERSION of the built library. */
 int dg_version(void);
 
 #ifdef __cplusplus
