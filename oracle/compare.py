@@ -20,7 +20,10 @@ terms, for results stored as FP32 where the stated factor alone must hold.
 The report gives the worst err/bound and where, RMSE and mean signed error
 (the sheratonhq.com deep dive, section 4.2, asks for error distribution, not
 only the maximum), the failure count, NaN agreement and whether the result is
-bitwise equal to the reference rounded to the output format.
+bitwise equal to the reference rounded to the output format.  NaN and Inf in
+the data propagate per IEEE (the cf-1.com article, section 5.3, tells of a
+NaN that a kernel must not hide): a NaN reference needs a NaN result, and an
+infinite one the same infinity.
 """
 from __future__ import annotations
 
@@ -104,13 +107,17 @@ def _report(C_gpu, want: np.ndarray, b: np.ndarray, rows, out_fmt: str) -> Compa
     assert got.shape == want.shape, (got.shape, want.shape)
     nan_g, nan_w = np.isnan(got), np.isnan(want)
     nan_mismatch = int(np.count_nonzero(nan_g != nan_w))
-    both = ~(nan_g | nan_w)
+    # An infinite reference (an Inf operand propagated per IEEE) is matched only
+    # by the same infinity; it takes no part in the error statistics.
+    inf_w = np.isinf(want) & ~nan_g
+    inf_mismatch = int(np.count_nonzero(inf_w & (got != want)))
+    both = ~(nan_g | nan_w | inf_w)
     err = np.where(both, got - want, 0.0)
     aerr = np.abs(err)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(both, np.where(b > 0, aerr / b, np.where(aerr > 0, np.inf, 0.0)), 0.0)
     ratio = np.where(np.isnan(ratio), np.inf, ratio)
-    fails = int(np.count_nonzero(ratio > 1.0)) + nan_mismatch
+    fails = int(np.count_nonzero(ratio > 1.0)) + nan_mismatch + inf_mismatch
     if ratio.size:
         idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
         mx = float(ratio[idx])
@@ -121,6 +128,6 @@ def _report(C_gpu, want: np.ndarray, b: np.ndarray, rows, out_fmt: str) -> Compa
     rmse = float(np.sqrt(np.sum(err * err) / nb))
     mean_err = float(np.sum(err) / nb)
     rounded = _round_to(want, out_fmt)
-    bitwise = bool(np.array_equal(got[both], rounded[both]) and nan_mismatch == 0)
+    bitwise = bool(np.array_equal(got[both], rounded[both]) and nan_mismatch == 0 and inf_mismatch == 0)
     return CompareReport(fails == 0, mx, argmax, rmse, mean_err, fails, nan_mismatch, bitwise,
                          int(got.size))

@@ -340,3 +340,72 @@ def test_comparator_flags_nan_mismatch_and_reports_stats():
     # "bitwise" means equal to the reference rounded (RNE) to the output format
     rep3 = oracle.compare(ref.C.astype(np.float32), ref, "f32", 1e-4)
     assert rep3.ok and rep3.bitwise
+
+
+# ----------------------------------------------------------------- special values (IEEE propagation)
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_nan_and_inf_propagate_like_a_python_loop(dtype):
+    # A NaN or an infinity in one operand reaches exactly the outputs it
+    # touches, as IEEE arithmetic says (the cf-1.com article, section 5.3: a
+    # NaN must show up, not vanish): checked against a pure-Python loop, whose
+    # floats are IEEE binary64.
+    M, N, K = 5, 6, 7
+    g = synth.rng(5)
+    A = synth.to_dtype(synth.draw(g, (M, K), "normal"), dtype)
+    B = synth.to_dtype(synth.draw(g, (K, N), "normal"), dtype)
+    A[1, 2] = float("nan")
+    A[3, 4] = float("inf")
+    B[0, 1] = float("-inf")
+    B[5, 4] = float("inf")
+    r = oracle.ref_gemm(A, B, None)
+    a, b = _vals(A), _vals(B)
+    for m in range(M):
+        for n in range(N):
+            p = 0.0
+            for k in range(K):
+                p += a[m][k] * b[k][n]
+            got = r.C[m, n]
+            assert (math.isnan(p) and math.isnan(got)) or got == p, (m, n, got, p)
+    assert np.isnan(r.C[1]).all()            # the NaN row
+    assert np.isinf(r.C[3, [0, 2, 3, 5]]).all()
+
+
+def test_fp8_nan_codes_propagate():
+    # E4M3FN has no infinity: 0x7F and 0xFF are its NaNs.
+    qa = torch.zeros(3, 128, dtype=torch.uint8)
+    qa[:] = 0x38          # 1.0
+    qa[1, 7] = 0x7F
+    qb = torch.full((128, 4), 0x38, dtype=torch.uint8)
+    qb[9, 2] = 0xFF
+    A, B = qa.view(E4M3), qb.view(E4M3)
+    r = oracle.ref_gemm(A, B, None, A_scale=torch.ones(3, 1), B_scale=torch.ones(1, 1))
+    want = np.full((3, 4), 128.0)
+    want[1, :] = np.nan
+    want[:, 2] = np.nan
+    assert np.array_equal(r.C, want, equal_nan=True)
+
+
+def test_fp16_subnormal_inputs_are_not_flushed():
+    # products of FP16 subnormals are exact in FP64: 2^-24 * 2^-24 summed K times
+    M, N, K = 2, 3, 16
+    A = torch.full((M, K), 2.0 ** -24, dtype=F16)
+    B = torch.full((K, N), 2.0 ** -24, dtype=F16)
+    B[:, 1] = 2.0 ** -15          # the largest binary exponent of the subnormal range
+    r = oracle.ref_gemm(A, B, None)
+    assert np.array_equal(r.C[:, 0], np.full(M, K * 2.0 ** -48))
+    assert np.array_equal(r.C[:, 1], np.full(M, K * 2.0 ** -39))
+
+
+def test_comparator_requires_the_same_infinity():
+    A = torch.ones(2, 4, dtype=BF16)
+    B = torch.ones(4, 3, dtype=BF16)
+    A[0, 1] = float("inf")
+    B[2, 2] = float("-inf")
+    ref = oracle.ref_gemm(A, B, None)
+    assert np.isinf(ref.C[0, 0]) and np.isnan(ref.C[0, 2]) and ref.C[1, 2] == -np.inf
+    assert oracle.compare(ref.C.copy(), ref, "f32", 1e-4).ok
+    for (i, j, v) in [(0, 0, -np.inf), (0, 0, 1e30), (1, 2, np.nan), (1, 2, np.inf), (0, 2, np.inf)]:
+        wrong = ref.C.copy()
+        wrong[i, j] = v
+        assert not oracle.compare(wrong, ref, "f32", 1e-4).ok, (i, j, v)
