@@ -97,8 +97,7 @@ def test_paths(dg, p, act):
     M, N, K, bl, al, want = p
     c = synth.gemm_case(M, N, K, BF16, BF16, seed=M + 3 * N + 7 * K, a_layout=al, b_layout=bl)
     c = synth.with_epilogue(c, act, BF16, "contig", seed=M + N)
-    rows = None if M <= 300 else sorted(set(r for r in [0, 1, 127, 128, 255, 256, 500, M - 1] if r < M))
-    check_epi(dg, c, rows=rows, want_in_plan=want)
+    check_epi(dg, c, want_in_plan=want)
 
 
 # ---------------------------------------------------------------- dtypes and bias layouts
@@ -182,21 +181,13 @@ def test_no_bias_no_act_is_bitwise_dg_gemm(dg, shape):
 def test_fp8(dg, shape, act):
     M, N, K = shape
     c = synth.fp8_case(M, N, K, seed=M + N, beta=0.25 if M == 100 else 0.0)
-    check_epi(dg, synth.with_epilogue(c, act, BF16, "contig", seed=14),
-              rows=None if M <= 256 else [0, 5, 127, 128, 511, M - 1])
+    check_epi(dg, synth.with_epilogue(c, act, BF16, "contig", seed=14))
 
 
 # ---------------------------------------------------------------- the workloads at full size
 
-def _sample_rows(M, n=24, seed=0):
-    g = np.random.default_rng(seed)
-    edge = [0, 1, M - 1, M // 2, min(63, M - 1), min(64, M - 1), min(255, M - 1), min(256, M - 1)]
-    return sorted(set(r for r in edge + g.integers(0, M, size=n).tolist() if 0 <= r < M))
-
-
 @pytest.mark.parametrize("name", ["c2a_gelu", "c3_gelu", "c4_gelu", "c5_128_gelu", "c5_4096_gelu"])
 def test_workload_full_size(dg, name):
     case = synth.config(name)
-    M = case.mnk[0]
-    _, d = check_epi(dg, case, rows=None if M <= 64 else _sample_rows(M, seed=len(name)))
+    _, d = check_epi(dg, case)     # every element of C
     assert torch.isfinite(d.C.float()).all()
