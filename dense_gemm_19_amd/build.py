@@ -45,18 +45,38 @@ def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
         t = os.path.getmtime(obj)
         if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
             return obj
-    flags = HIP_FLAGS if src.endswith(".hip") else HOST_FLAGS
+    hip = src.endswith(".hip")
+    flags = HIP_FLAGS + ["-Rpass-analysis=kernel-resource-usage"] if hip else HOST_FLAGS
     cmd = [HIPCC] + flags + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
+    lines = r.stderr.splitlines()
     # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in lines if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{err}")
+    if hip:
+        spills = _scratch_kernels(lines)
+        if spills:
+            os.remove(obj)
+            raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {spills}")
     if err.strip() and verbose:
         print(err)
     return obj
+
+
+def _scratch_kernels(remarks) -> list:
+    """Kernels whose resource-usage remark reports scratch (spilled registers)."""
+    out, name = [], None
+    for l in remarks:
+        if "remark: Function Name:" in l:
+            name = l.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in l and name:
+            n = int(l.split("ScratchSize [bytes/lane]:")[1].split("[")[0].strip())
+            if n > 0:
+                out.append(f"{name} ({n} bytes/lane)")
+    return out
 
 
 def build(verbose: bool = False, jobs: int | None = None, incremental: bool = False) -> str:

@@ -538,8 +538,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         finish_any();
         return;
     }
-    // split K: publish this piece's partial tile (agent-scope stores are
-    // coherent across the XCDs' L2 caches), wait for the stores, take a ticket.
+    // split K: publish this piece's partial tile with agent-scope stores, wait
+    // for the stores, take a ticket (take_last_ticket: the last piece then
+    // sees every partial).
     // Partials of split tile w = t - dp_tiles live at
     //   ws[((w * S + q) * NW + wave) * (TM * TN * 4) + element) * 64 + lane]:
     // every thread writes and reads its own elements (the last piece runs the
@@ -560,9 +561,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int tile = tm * p.tiles_n + tn;
-    if (tid == 0)
-        is_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  S - 1;
+    if (tid == 0) is_last = take_last_ticket(p.counters + tile, S);
     __syncthreads();
     if (!is_last) return;
     // The sum runs over s = 0..S-1 in order, this workgroup's own partial

@@ -234,36 +234,7 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[TM][TN], const Mfm
     // its values, then its stores.  A load, or a use of a loaded value, placed
     // after a store would also wait for that store (one counter tracks both),
     // and each element would pay a memory round trip.
-    if constexpr (TM * TN > 16) {
-        // The 256x256 tile's accumulators fill the registers: element by
-        // element (batching here spills the accumulators to scratch).
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = nb + 16 * j;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = mb + 16 * i + e;
-                    if (m < p.M && n < p.N) {
-                        const float a = acc[i][j][e];
-                        if (OUTK < 0) {
-                            p.ws[((int64_t)z * p.M + m) * p.N + n] = a;
-                        } else {
-                            char *q = ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs;
-                            float v = ep.alpha * a;
-                            if (ep.beta != 0.0f) v = fmaf(ep.beta, load_out(q, OUTK), v);
-                            if (FUSED) {
-                                if (ep.bias) v += bias[j];
-                                v = activate(ep.act, v);
-                            }
-                            store_out(q, OUTK, v);
-                        }
-                    }
-                }
-            }
-        return;
-    }
+    static_assert(TM * TN <= 16, "tiles of at most 64 accumulators per lane");
     constexpr int JB = TN < 4 ? TN : 4;   // 16-column blocks per batch (registers: 2 x 16 values)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -467,7 +438,6 @@ hipError_t launch_modes(int am, int bm, const MfmaArgs &a, hipStream_t s) {
 template <int IN, int SLOW>
 hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
     switch (tile) {
-    case T256x256: return launch_modes<IN, 256, 256, SLOW>(am, bm, a, s);
     case T128x128: return launch_modes<IN, 128, 128, SLOW>(am, bm, a, s);
     case T64x64: return launch_modes<IN, 64, 64, SLOW>(am, bm, a, s);
     case T128x64: return launch_modes<IN, 128, 64, SLOW>(am, bm, a, s);

@@ -107,6 +107,10 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
         pl.sk_kc = (int)std::min<int64_t>(cdiv(kps, sweep) * sweep, kc_max);
         pl.lds_bytes = skinny_bn_lds(mmax, pl.sk_kc);
         pl.counters = pl.splits > 1 ? pl.sk_grid_x : 0;
+        // A staged with 16-byte loads: K-contiguous 16-byte-aligned rows, and K a
+        // multiple of 8 so that no piece crosses the end of a row
+        pl.sk_a_vec = A.cols_contig() && A.cs == A.esize && A.align_ptr >= 16 && (p.M <= 1 || A.align_rs >= 16) &&
+                      p.K % 8 == 0;
         return true;
     }
     // B K-contiguous (e.g. a transposed cache): one wave per column.
@@ -193,20 +197,21 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
         if (c.tile >= 0) tile = c.tile;
     } else if (!pl.slow) {
         // general kernel (register-staged loads, K tails): tiles it implements
-        const int order[] = {T256x256, T128x128, T128x64, T64x64};
+        // (no 256x256: its accumulators and staging registers would spill)
+        const int order[] = {T128x128, T128x64, T64x64};
         int best = T64x64;
         int64_t best_tiles = -1;
         bool found = false;
         for (int t : order) {
-            if (p.fp8 && t == T256x256) continue;
             if (tile_eff(p.M, p.N, t) < 0.75 && t != T64x64) continue;
             const int64_t nt = tile_count(p.M, p.N, t);
             if (nt >= d.cus) { tile = t; found = true; break; }
             if (nt > best_tiles) { best_tiles = nt; best = t; }
         }
         if (!found) tile = best;
-        if (overrides().force_tile >= 0 && overrides().force_tile != T64x128) tile = overrides().force_tile;
-        if (c.tile >= 0 && c.tile != T64x128 && !(p.fp8 && c.tile == T256x256)) tile = c.tile;
+        const auto general_has = [](int t) { return t != T64x128 && t != T256x256; };
+        if (overrides().force_tile >= 0 && general_has(overrides().force_tile)) tile = overrides().force_tile;
+        if (c.tile >= 0 && general_has(c.tile)) tile = c.tile;
     }
     // K split for that tile.
     int64_t S = 1;
@@ -474,10 +479,9 @@ std::vector<PlanChoice> candidate_choices(const Problem &p, const Device &d) {
     } else if (def.path == Path::Mfma) {
         std::vector<int> tiles;
         if (def.dtl) tiles = {T256x256, T128x128, T128x64, T64x64, T64x128};
-        else if (!def.slow) tiles = {T256x256, T128x128, T128x64, T64x64};
+        else if (!def.slow) tiles = {T128x128, T128x64, T64x64};
         else tiles = {-1};
         for (int t : tiles) {
-            if (t >= 0 && p.fp8 && t == T256x256 && !def.dtl) continue;   // (the register-staged kernel spills)
             // no tile larger than the matrix in either dimension
             if (t >= 0 && (mfma_tile_bm(t) > std::max<int64_t>(64, p.M) || mfma_tile_bn(t) > std::max<int64_t>(64, p.N)))
                 continue;

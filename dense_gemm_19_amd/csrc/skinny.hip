@@ -133,9 +133,12 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
         u32x4 v[BN_U];
 
         // Stage A[0..MMAX)[c0..c1) in LDS (rows >= M and k >= c1 as zeros).  With
-        // A rows K-contiguous, every thread first issues one 16-byte piece of A
-        // (threads past the end read the zero block and write a spare LDS slot),
-        // then the 8 loads of B, and only then stores A to LDS.
+        // A rows K-contiguous and 16-byte aligned and K a multiple of 8 (a_vec;
+        // then every chunk length is a multiple of 8 and a 16-byte piece that
+        // starts inside the chunk ends inside it), every thread first issues one
+        // 16-byte piece of A (threads past the end read the zero block and
+        // write a spare LDS slot), then the 8 loads of B, and only then stores A
+        // to LDS.
         const int achunks = MMAX * (p.kc / 8);
         auto a_chunk = [&](int idx, int &off) {
             const int m = idx / (p.kc / 8), k = (idx - m * (p.kc / 8)) * 8;
@@ -144,17 +147,6 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
             const char *q = in ? p.A + (int64_t)m * p.a_rs + (int64_t)(c0 + k) * 2
                                : reinterpret_cast<const char *>(&g_zero16);
             return *(const gu32x4 *)q;
-        };
-        auto a_fix = [&](u32x4 x, int off) {   // zero the values beyond the chunk end
-            const int k = off % p.kc;
-            if (k + 8 > clen) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int e = k + 2 * q;
-                    x[q] &= (e >= clen ? 0u : e + 1 >= clen ? 0xffffu : 0xffffffffu);
-                }
-            }
-            return x;
         };
         int a_off = 0;
         u32x4 a_first = u32x4{0u, 0u, 0u, 0u};
@@ -168,11 +160,11 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
         __builtin_amdgcn_sched_barrier(0);
         if (c0 != kb) __syncthreads();   // the previous chunk's A is no longer read
         if (p.a_vec) {
-            *reinterpret_cast<u32x4 *>(la + a_off) = a_fix(a_first, a_off);
+            *reinterpret_cast<u32x4 *>(la + a_off) = a_first;
             for (int idx = tid + BN_NT; idx < achunks; idx += BN_NT) {
                 int off;
                 const u32x4 x = a_chunk(idx, off);
-                *reinterpret_cast<u32x4 *>(la + off) = a_fix(x, off);
+                *reinterpret_cast<u32x4 *>(la + off) = x;
             }
         } else {
             for (int idx = tid; idx < MMAX * p.kc; idx += BN_NT) {
@@ -258,15 +250,13 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
     // adds the S partials in the order s = 0..S-1 (so the bits do not depend on
     // which workgroup finishes last), applies the epilogue, and re-arms the
     // slab's counter for the next call on this stream.  The partials are
-    // written and read with agent-scope atomic accesses (coherent across the
-    // XCDs without writing back or invalidating whole L2 caches); each thread
-    // waits until its partial stores have completed before the workgroup takes
-    // its ticket, so the workgroup holding the last ticket sees every partial.
+    // written and read with agent-scope atomic accesses; each thread waits
+    // until its partial stores have completed, then the workgroup takes its
+    // ticket (take_last_ticket states why the workgroup holding the last
+    // ticket sees every partial).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
-        is_last = __hip_atomic_fetch_add(p.counters + slab, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
+    if (tid == 0) is_last = take_last_ticket(p.counters + slab, p.splits);
     __syncthreads();
     if (!is_last) return;
     const int64_t plane = (int64_t)p.M * p.N;
