@@ -34,7 +34,7 @@ _DTYPE = {torch.float32: DG_F32, torch.float16: DG_F16, torch.bfloat16: DG_BF16,
 STATUS = ["DG_SUCCESS", "DG_ERR_NULL", "DG_ERR_NDIM", "DG_ERR_STRIDE", "DG_ERR_SHAPE_MISMATCH",
           "DG_ERR_DTYPE", "DG_ERR_MISALIGNED", "DG_ERR_ALIAS", "DG_ERR_NONFINITE_SCALAR",
           "DG_ERR_OVERFLOW", "DG_ERR_UNSUPPORTED_VIEW", "DG_ERR_POINTER", "DG_ERR_ARCH",
-          "DG_ERR_HIP", "DG_ERR_INVALID_ARG"]
+          "DG_ERR_HIP", "DG_ERR_INVALID_ARG", "DG_ERR_SCRATCH"]
 
 
 class DGError(RuntimeError):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_candidates.argtypes = [P, P, P, P, P, PC, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         L.dg_gemm_with_choice.argtypes = [P, P, P, P, P, PC, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
         L.dg_gemm_tune.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.POINTER(TuneResult), ctypes.c_void_p]
+        L.dg_gemm_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+        L.dg_gemm_noalloc.restype = ctypes.c_int
         L.dg_tune_save.argtypes = [ctypes.c_char_p]
         L.dg_tune_load.argtypes = [ctypes.c_char_p]
         for f in ("dg_gemm_candidates", "dg_gemm_with_choice", "dg_gemm_tune", "dg_tune_save", "dg_tune_load"):
@@ -249,6 +251,13 @@ def gemm_with_choice(A, B, C, choice, alpha: float = 1.0, beta: float = 0.0, A_s
     vs, refs = _opt_views(A, A_scale, B, B_scale, C)
     c = PlanChoice(*choice)
     _check(lib().dg_gemm_with_choice(*refs, ctypes.byref(c), alpha, beta, _stream(stream)), "dg_gemm_with_choice")
+    return C
+
+
+def gemm_noalloc(A, B, C, alpha: float = 1.0, beta: float = 0.0, A_scale=None, B_scale=None, stream=None):
+    """dg_gemm / dg_gemm_fp8 on the library's fixed split-K scratch (allocates nothing); returns C."""
+    vs, refs = _opt_views(A, A_scale, B, B_scale, C)
+    _check(lib().dg_gemm_noalloc(*refs, alpha, beta, _stream(stream)), "dg_gemm_noalloc")
     return C
 
 

@@ -29,7 +29,7 @@ EXTRA_FLAGS = {"gemm_dtl_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 HIP_SOURCES = ["gemm_mfma.hip", "gemm_dtl_f16.hip", "gemm_dtl_bf16.hip", "gemm_dtl_f8.hip", "skinny.hip",
-               "epilogue.hip", "calib.hip", "quant.hip"]
+               "epilogue.hip", "calib.hip", "quant.hip", "noalloc.hip"]
 HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp", "gemm_dtl.cpp"]
 
 

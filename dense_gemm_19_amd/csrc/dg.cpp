@@ -723,6 +723,34 @@ dg_status tune_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
     return DG_SUCCESS;
 }
 
+// No-allocation GEMM (dg_gemm_noalloc): the plan dg_gemm / dg_gemm_fp8 would
+// run, on the fixed scratch of noalloc.hip instead of the stream's workspace.
+// Nothing here allocates device memory.
+dg_status noalloc_entry(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
+                        const dg_view *C, float alpha, float beta, hipStream_t stream) {
+    Problem p;
+    dg_status st = validate_any(A, SA, B, SB, C, alpha, beta, &p);
+    if (st != DG_SUCCESS) return st;
+    Device d;
+    if ((st = current_device(&d, true)) != DG_SUCCESS) return st;
+    if (!d.gfx950) return DG_ERR_ARCH;
+    if (env_on("DG_CHECK_POINTERS")) {
+        const Mat *ms[] = {&p.A, &p.B, &p.C, p.fp8 ? &p.SA : nullptr, p.fp8 ? &p.SB : nullptr};
+        for (const Mat *m : ms)
+            if (m && !m->empty() && (st = check_pointer(m->ptr)) != DG_SUCCESS) return st;
+    }
+    const Plan pl = cached_plan(p, d);
+    Scratch sc;
+    if (pl.splits > 1) {
+        if (pl.ws_bytes > NOALLOC_WS_BYTES || pl.counters > NOALLOC_COUNTERS) return DG_ERR_SCRATCH;
+        if (noalloc_scratch(stream, &sc.ws, &sc.counters) != hipSuccess) {
+            (void)hipGetLastError();
+            return DG_ERR_HIP;
+        }
+    }
+    return launch_plan(p, pl, sc, stream);
+}
+
 // FP8 quantizer (dg_quant_fp8): validate X, Q, S as include/dg.h states, then
 // launch one 256-thread workgroup per 128 x 128 tile of X.
 dg_status quant_entry(const dg_view *X, const dg_view *Q, const dg_view *S, int mode, hipStream_t stream) {
@@ -773,6 +801,11 @@ extern "C" {
 dg_status dg_quant_fp8(const dg_view *X, const dg_view *Q, const dg_view *S, dg_quant_mode mode,
                        hipStream_t stream) {
     return dg::quant_entry(X, Q, S, (int)mode, stream);
+}
+
+dg_status dg_gemm_noalloc(const dg_view *A, const dg_view *A_scale, const dg_view *B, const dg_view *B_scale,
+                          const dg_view *C, float alpha, float beta, hipStream_t stream) {
+    return dg::noalloc_entry(A, A_scale, B, B_scale, C, alpha, beta, stream);
 }
 
 dg_status dg_gemm_candidates(const dg_view *A, const dg_view *A_scale, const dg_view *B, const dg_view *B_scale,
@@ -865,6 +898,7 @@ const char *dg_status_str(dg_status s) {
     case DG_ERR_ARCH: return "DG_ERR_ARCH";
     case DG_ERR_HIP: return "DG_ERR_HIP";
     case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
+    case DG_ERR_SCRATCH: return "DG_ERR_SCRATCH";
     }
     return "DG_ERR_UNKNOWN";
 }

@@ -157,5 +157,13 @@ hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);
 hipError_t launch_fill_zero(int *p, int64_t n, hipStream_t stream);
 
+// Fixed split-K scratch of dg_gemm_noalloc (noalloc.hip): 16 MiB of FP32
+// partials and 16384 arrival counters per device, held from module load until
+// the process ends.  noalloc_scratch returns the current device's addresses
+// (taken with hipGetSymbolAddress at its first call on that device, which also
+// zeroes the counters on `stream`).
+constexpr size_t NOALLOC_WS_BYTES = size_t(16) << 20;
+constexpr int NOALLOC_COUNTERS = 16384;
+hipError_t noalloc_scratch(hipStream_t stream, float **ws, int **counters);
 
 }  // namespace dg

@@ -89,7 +89,9 @@ typedef enum {
     DG_ERR_POINTER = 11,          /* not a device pointer (checked only if DG_CHECK_POINTERS=1) */
     DG_ERR_ARCH = 12,             /* current device is not gfx950 */
     DG_ERR_HIP = 13,              /* a HIP runtime call or kernel launch failed */
-    DG_ERR_INVALID_ARG = 14       /* other invalid argument (e.g. a null output buffer) */
+    DG_ERR_INVALID_ARG = 14,      /* other invalid argument (e.g. a null output buffer) */
+    DG_ERR_SCRATCH = 15           /* dg_gemm_noalloc: the plan needs more split-K scratch
+                                     than the fixed buffer holds */
 } dg_status;
 
 /* A tensor view: up to 4 dims, strides in BYTES (kwkr.cn article, section 3.2). */
@@ -282,6 +284,29 @@ dg_status dg_tune_load(const char *path);
 void dg_tune_clear(void);
 /* Number of tuned plans held. */
 int32_t dg_tune_count(void);
+
+/*
+ * dg_gemm / dg_gemm_fp8 for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  A_scale and B_scale: both NULL for FP16/BF16 inputs, both given
+ * for FP8 (dg_gemm_fp8's rules; one NULL and not the other is DG_ERR_NULL).
+ * Same plan, kernels, results (bit for bit), bound and errors as dg_gemm /
+ * dg_gemm_fp8, but the split-K scratch is a fixed device array inside the
+ * library instead of the stream's workspace, and the call allocates nothing
+ * (no hipMalloc, hipMallocAsync or allocating library routine).
+ *  - The fixed array holds 16 MiB of FP32 partial sums and 16384 arrival
+ *    counters per device, from the library's load until the process ends.  A
+ *    problem whose plan needs more returns DG_ERR_SCRATCH and enqueues nothing.
+ *  - Every dg_gemm_noalloc call on one device shares that device's array: two
+ *    calls whose work overlaps in time on one device (different streams, or
+ *    different host threads with no ordering between them) race and may
+ *    return wrong results.  Calls ordered on one stream are safe.
+ *  - The first call on a device enqueues a zeroing of the counters on its
+ *    stream; every kernel that uses them leaves them at zero.
+ */
+dg_status dg_gemm_noalloc(const dg_view *A, const dg_view *A_scale, const dg_view *B,
+                          const dg_view *B_scale, const dg_view *C, float alpha, float beta,
+                          hipStream_t stream);
 
 /*
  * Validate the arguments of dg_gemm exactly as dg_gemm does and write a

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
     assert dg.version() == 10000
     assert dg.status_str(7) == "DG_ERR_ALIAS"
+    assert dg.status_str(15) == "DG_ERR_SCRATCH"
 
 
 def mat(ptr, rows, cols, rs, cs, dt=DG_BF16):
