@@ -52,6 +52,35 @@ __device__ __forceinline__ void store_out(char *p, int kind, float v) {
     else *reinterpret_cast<uint16_t *>(p) = f32_to_f16_bits(v);
 }
 
+// Four adjacent output elements (p 4-element aligned, in the C dtype), as one
+// vector access.
+__device__ __forceinline__ f32x4 load_out4(const char *p, int kind) {
+    if (kind == OUT_F32) return *reinterpret_cast<const f32x4 *>(p);
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint16_t b = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        v[e] = kind == OUT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+    }
+    return v;
+}
+
+__device__ __forceinline__ void store_out4(char *p, int kind, const float (&v)[4]) {
+    if (kind == OUT_F32) {
+        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        return;
+    }
+    u32x2 w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = kind == OUT_BF16 ? f32_to_bf16_bits(v[2 * h]) : f32_to_f16_bits(v[2 * h]);
+        const uint32_t hi = kind == OUT_BF16 ? f32_to_bf16_bits(v[2 * h + 1]) : f32_to_f16_bits(v[2 * h + 1]);
+        w[h] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x2 *>(p) = w;
+}
+
 // Sum of S split-K partials, ((p0 + p1) + p2) + ... always in this order, with
 // the loads issued 8 at a time so that their latencies overlap (a runtime-bounded
 // loop would otherwise wait for each load before issuing the next).

@@ -256,6 +256,8 @@ Epilogue make_epi(const Problem &p) {
     e.bias_s = p.bias.cs;
     e.bias_kind = p.bias.dtype;   // dg_dtype and OutKind agree for F32 / F16 / BF16
     e.act = p.act;
+    const int64_t es = p.C.esize, v = 4 * es;
+    e.vec4 = p.C.cs == es && reinterpret_cast<uintptr_t>(p.C.ptr) % v == 0 && (p.C.rows <= 1 || p.C.rs % v == 0);
     return e;
 }
 

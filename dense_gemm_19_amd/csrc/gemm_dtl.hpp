@@ -203,6 +203,10 @@ __device__ __forceinline__ i32x8 frag8(const char *lds, int rb, int lane) {
     return out;
 }
 
+// The kernel passes its B fragment as the instruction's first operand and its A
+// fragment as the second, so each 16 x 16 result block comes out transposed:
+// lane l holds row l % 16 and the 4 adjacent columns 4 (l / 16) .. + 3.  A lane
+// then needs one FP8 row scale per block, and stores 4 adjacent elements of C.
 template <int IN>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     if (IN == IN_BF16)
@@ -308,9 +312,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // FP8 scale sources of this thread's lane for the staging loads
+    // FP8 scale sources of this thread's lane for the staging loads.  The BM
+    // row scales of a stage sit in LDS grouped by row mod 16: row r at float
+    // (r % 16) * (BM / 16) + r / 16, so that a lane finds the scales of its
+    // rows (one per 16-row block, see compute) side by side.  The loader lane
+    // filling float p fetches the row stored there.
     const int NBLK = (p.N + 127) >> 7;
-    const int sa_row = min(m0 + 64 * (wave % (F8 ? BM / 64 : 1)) + lane, p.M - 1);
+    const int sa_pos = 64 * (wave % (F8 ? BM / 64 : 1)) + lane;
+    const int sa_row = min(m0 + (sa_pos % (BM / 16)) * 16 + sa_pos / (BM / 16), p.M - 1);
     const int sb_blk = min((n0 >> 7) + lane, NBLK - 1);
 
     // Source addresses are computed once; each tile only adds a uniform K offset.
@@ -340,8 +349,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     auto compute = [&](const char *la) __attribute__((always_inline)) {
         const char *lb = la + A_BYTES;
         if constexpr (F8) {
-            const float *lsa = reinterpret_cast<const float *>(la + SA_OFF);
+            // This lane's rows are wm * WTM + 16 i + lane % 16 (the products are
+            // formed transposed, see mma), so it needs one row scale per 16-row
+            // block: TM floats side by side in the stage's scale layout.
+            const float *lsa = reinterpret_cast<const float *>(la + SA_OFF) + (lane & 15) * (BM / 16) + wm * TM;
             const float sb = reinterpret_cast<const float *>(la + SB_OFF)[(wn * WTN) >> 7];
+            float sc[TM];
+            if constexpr (TM % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < TM; q += 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(lsa + q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[q + e] = v[e] * sb;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < TM; ++q) sc[q] = lsa[q] * sb;
+            }
             i32x8 fb[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j) fb[j] = frag8<BMODE, BN>(lb, wn * WTN + 16 * j, lane);
@@ -351,27 +375,30 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             // t + 1 and t + 2 are issued, so the vector ALUs work while the matrix
             // core does.
             constexpr int PL = 2;   // promotion lag, in blocks
-            i32x8 fa;
-            f32x4 s4[TM], blk[TM * TN];
+            // Each step is fenced (sched_barrier) so that the compiler keeps the
+            // order written here: the matrix instruction of block t, then the
+            // promotion of block t - PL, whose sums are complete by then; left
+            // free, it pulls each block's promotion up behind its own matrix
+            // instruction and pads the wait with nops.  The A fragment of the
+            // next 16-row block is read TN blocks ahead of its first use.
+            i32x8 fa = frag8<AMODE, BM>(la, wm * WTM, lane), fa_next = fa;
+            f32x4 blk[PL + 1];
 #pragma unroll
             for (int t = 0; t < TM * TN + PL; ++t) {
                 if (t < TM * TN) {
                     const int i = t / TN, j = t % TN;
-                    if (j == 0) {
-                        fa = frag8<AMODE, BM>(la, wm * WTM + 16 * i, lane);
-                        const f32x4 sa4 = *reinterpret_cast<const f32x4 *>(lsa + wm * WTM + 16 * i + 4 * (lane >> 4));
-                        s4[i] = sa4 * sb;
-                    }
-                    blk[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        fa, fb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (j == 0 && i + 1 < TM) fa_next = frag8<AMODE, BM>(la, wm * WTM + 16 * (i + 1), lane);
+                    blk[t % (PL + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    if (j == TN - 1) fa = fa_next;
                 }
                 if (t >= PL) {
                     const int u = t - PL, pi = u / TN, pj = u % TN;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[pi][pj][e] = fmaf(s4[pi][e], blk[u][e], acc[pi][pj][e]);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    for (int e = 0; e < 4; ++e)
+                        acc[pi][pj][e] = fmaf(sc[pi], blk[u % (PL + 1)][e], acc[pi][pj][e]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             // The wave's B fragments of a K step stay in registers; A fragments
@@ -399,7 +426,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
                 if (t + PD < STEPS) read_step(t + PD);
                 const int ks = t / TM, i = t % TM;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<IN>(fa[t % (PD + 1)], fb[ks][j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<IN>(fb[ks][j], fa[t % (PD + 1)], acc[i][j]);
                 __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
             }
         }
@@ -459,8 +486,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         }
     }
 
-    // ---- epilogue: element (i, j, e) of a wave is C[mb + 16i + e][nb + 16j]
-    const int mb = m0 + wm * WTM + 4 * (lane >> 4), nb = n0 + wn * WTN + (lane & 15);
+    // ---- epilogue: element (i, j, e) of a wave is C[mr + 16i][nc + 16j + e]
+    // (the products are formed transposed: a lane holds 4 adjacent columns of
+    // one row per 16 x 16 block)
+    const int mr = m0 + wm * WTM + (lane & 15), nc = n0 + wn * WTN + 4 * (lane >> 4);
     const Epilogue &ep = p.epi;
     // FUSED: bias (read once per column) and activation after alpha/beta.
     // The value stored at (m, n): alpha * acc (+ beta * C_in) (+ bias), activated;
@@ -476,28 +505,41 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     };
     auto finish = [&](auto OUTK, auto FUSED) __attribute__((always_inline)) {
         constexpr int ok = decltype(OUTK)::value;
-        float bias[TN];
+        constexpr bool fused = decltype(FUSED)::value;
+        float bias[TN][4];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            bias[j] = decltype(FUSED)::value && ep.bias && nb + 16 * j < p.N ? load_bias(ep, nb + 16 * j) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = nc + 16 * j + e;
+                bias[j][e] = fused && ep.bias && n < p.N ? load_bias(ep, n) : 0.0f;
+            }
         // One 16-row block at a time: all of the block's C_in loads (beta != 0),
         // then all of its values, then all of its stores.  A load or a use of a
         // loaded value placed after a store would wait for that store too (the
         // counter that tracks loads counts stores), and each element would pay
         // a memory round trip; so would a load inside a per-element branch.
+        // Where C's rows are contiguous and 4-element aligned (ep.vec4), each
+        // lane's 4 adjacent columns go in one vector load or store.
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            const int m = mr + 16 * i;
+            // clamped into the matrix: every lane loads (no branch per element);
+            // values past the edge are never stored
+            const char *crow = ep.C + (int64_t)min(m, p.M - 1) * ep.c_rs;
             float cin[TN][4], out[TN][4];
             if (ep.beta != 0.0f) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int n = nb + 16 * j;
+                    const int n = nc + 16 * j;
+                    if (ep.vec4 && n + 3 < p.N) {
+                        const f32x4 v = load_out4(crow + (int64_t)n * ep.c_cs, ok);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        // clamped into the matrix: every lane loads (no branch
-                        // per element); values past the edge are never stored
-                        const int m = min(mb + 16 * i + e, p.M - 1), nc = min(n, p.N - 1);
-                        cin[j][e] = load_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)nc * ep.c_cs, ok);
+                        for (int e = 0; e < 4; ++e) cin[j][e] = v[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            cin[j][e] = load_out(crow + (int64_t)min(n + e, p.N - 1) * ep.c_cs, ok);
                     }
                 }
             }
@@ -505,18 +547,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    out[j][e] = value(FUSED, acc[i][j][e], bias[j], cin[j][e]);
+                    out[j][e] = value(FUSED, acc[i][j][e], bias[j][e], cin[j][e]);
                     // pins the value here: the compiler would otherwise sink its
                     // computation into the store's branch, after earlier stores
                     asm volatile("" : "+v"(out[j][e]));
                 }
+            if (m < p.M) {
+                char *row = ep.C + (int64_t)m * ep.c_rs;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = nb + 16 * j;
+                for (int j = 0; j < TN; ++j) {
+                    const int n = nc + 16 * j;
+                    if (ep.vec4 && n + 3 < p.N) {
+                        store_out4(row + (int64_t)n * ep.c_cs, ok, out[j]);
+                    } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = mb + 16 * i + e;
-                    if (m < p.M && n < p.N) store_out(ep.C + (int64_t)m * ep.c_rs + (int64_t)n * ep.c_cs, ok, out[j][e]);
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) store_out(row + (int64_t)(n + e) * ep.c_cs, ok, out[j][e]);
+                    }
                 }
             }
         }

@@ -42,6 +42,8 @@ struct Epilogue {
     int64_t bias_s;     // bytes between consecutive bias elements (0: one value for every column)
     int bias_kind;      // OutKind numbering: OUT_F32 / OUT_F16 / OUT_BF16
     int act;            // Act
+    int vec4;           // C's rows are contiguous and 4-element aligned (c_cs == element size,
+                        // C and c_rs multiples of 4 elements): 4 adjacent columns in one access
     constexpr bool plain() const { return bias == nullptr && act == ACT_NONE; }
 };
 
