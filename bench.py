@@ -23,7 +23,10 @@ The JSON line also carries:
                 8 TB/s HBM3E peak, and the
                 HBM traffic read from rocprofv3 counters (profiles/), or null when
                 the kernel source changed since they were taken;
-  cpu_baseline  the FP64 CPU oracle on the same step, on the host's cores;
+  cpu_baseline  the FP64 CPU oracle on the same step, on the host's cores, with
+                the CPU model and, under `configs`, the oracle timed on every
+                workload (median of 3 for M <= 64, one run otherwise, and the
+                64x512x512 problem on one core as well);
   measured_peaks  what this device sustains under ideal code, measured in the
                 same run (register-only MFMA loops, a 2 GiB streaming read, the
                 launch floor); roofline.frac_of_measured and each config's
@@ -365,7 +368,7 @@ def time_config(dg, name, reps=None, trials=5, tune=False):
                         "speedup": round(t / tt, 4), "tune_ms": round(r["tune_ms"], 2),
                         "candidates": r["candidates"], "chosen": r["chosen"],
                         "tuner_default_us": round(r["default_us"], 3), "tuner_best_us": round(r["best_us"], 3),
-                        "plan": r["plan"].split(" | ")[0].split(" path=")[1],
+                        "plan": r["plan"].split(" | ")[0].split(" path=")[1], "sets": r["sets"],
                         "calls_to_amortize": (round(r["tune_ms"] * 1e-3 / (t - tt)) if tt < t else None)}
         dg.tune_clear()
     del sets
@@ -410,7 +413,50 @@ def cpu_baseline(cases, budget_s=12.0):
     return {"value": round(nbytes * reps / t_total / 1e9, 4), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} whole steps (x.W1 1x4096x14336 + q.K_cache^T 1x4096x128, BF16 in, "
-                      f"FP64 arithmetic) in {t_total:.1f} s"}
+                      f"FP64 arithmetic) in {t_total:.1f} s",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_configs(names=("c1", "c2a", "c2b", "c3", "c4", "c5_128", "c5_4096")):
+    """The oracle timed on every workload, on all host threads: the small
+    shapes (M <= 64) as the median of 3 runs, the others one run each, and the
+    FP16 64x512x512 problem once more on one core.  Seconds and FP64 GFLOP/s
+    (2MNK per run; the sum of |a*b| the bound needs is formed in the same pass)."""
+    import statistics
+    import oracle
+    import synth
+    out = {}
+    for name in names:
+        c = synth.config(name)
+        hv = [None if t is None else oracle.host_view(t) for t in (c.A, c.B, c.A_scale, c.B_scale)]
+        cin = oracle.host_view(c.C) if c.beta != 0 else None
+        M, N, K = c.mnk
+        runs = 3 if M <= 64 else 1
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            oracle.ref_gemm(hv[0], hv[1], cin, c.alpha, c.beta, A_scale=hv[2], B_scale=hv[3])
+            ts.append(time.perf_counter() - t0)
+        t = statistics.median(ts)
+        out[name] = {"s": round(t, 4), "gflops_fp64": round(2.0 * M * N * K / t / 1e9, 2), "runs": runs,
+                     "threads": oracle.num_threads()}
+        if name == "c1":
+            t0 = time.perf_counter()
+            oracle.ref_gemm(hv[0], hv[1], cin, c.alpha, c.beta, nthreads=1)
+            t1 = time.perf_counter() - t0
+            out["c1_one_core"] = {"s": round(t1, 4), "gflops_fp64": round(2.0 * M * N * K / t1 / 1e9, 2),
+                                  "runs": 1, "threads": 1}
+    return out
 
 
 def measured_peaks(dg, nbytes=2 << 30):
@@ -592,6 +638,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline([c2a, c2b])
+        cpu["configs"] = cpu_oracle_configs()
         log("cpu baseline:", json.dumps(cpu))
 
     out = {

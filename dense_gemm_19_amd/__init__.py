@@ -62,7 +62,8 @@ class PlanChoice(ctypes.Structure):
 
 class TuneResult(ctypes.Structure):
     _fields_ = [("default_us", ctypes.c_double), ("best_us", ctypes.c_double), ("tune_ms", ctypes.c_double),
-                ("candidates", ctypes.c_int32), ("chosen", ctypes.c_int32), ("plan", ctypes.c_char * 512)]
+                ("candidates", ctypes.c_int32), ("chosen", ctypes.c_int32), ("sets", ctypes.c_int32),
+                ("plan", ctypes.c_char * 512)]
 
 
 _lib = None
@@ -267,7 +268,7 @@ def tune(A, B, C, A_scale=None, B_scale=None, reps: int = 0, stream=None) -> dic
     r = TuneResult()
     _check(lib().dg_gemm_tune(*refs, reps, ctypes.byref(r), _stream(stream)), "dg_gemm_tune")
     return {"default_us": r.default_us, "best_us": r.best_us, "tune_ms": r.tune_ms,
-            "candidates": r.candidates, "chosen": r.chosen, "plan": r.plan.decode()}
+            "candidates": r.candidates, "chosen": r.chosen, "sets": r.sets, "plan": r.plan.decode()}
 
 
 def tune_save(path: str):

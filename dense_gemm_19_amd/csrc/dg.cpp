@@ -648,6 +648,59 @@ dg_status with_choice_entry(const dg_view *A, const dg_view *SA, const dg_view *
     return run_plan(p, select_plan(p, d, from_abi(*choice)), stream);
 }
 
+// Operand copies for timing candidate plans: enough distinct sets of A, B, C
+// (and the FP8 scales) that the launches of a timing loop read their operands
+// from HBM, as the GEMM does in a workload, not from the 256 MB last-level
+// cache (>= 1 GiB in total, at most 64 sets; a problem of >= 512 MB uses its
+// own buffers only).  Set 0 is the caller's buffers.  Each copy keeps its
+// operand's address modulo 256, so every set gets the same plan.
+struct RotationSets {
+    std::vector<void *> bufs;
+    std::vector<Problem> probs;
+    RotationSets() = default;
+    RotationSets(const RotationSets &) = delete;
+    RotationSets &operator=(const RotationSets &) = delete;
+    ~RotationSets() {
+        for (void *b : bufs) (void)hipFree(b);
+    }
+};
+
+hipError_t make_rotation(const Problem &p, hipStream_t stream, RotationSets *r) {
+    auto ops = [](Problem &q) {
+        return std::vector<Mat *>{&q.A, &q.B, &q.C, q.fp8 ? &q.SA : nullptr, q.fp8 ? &q.SB : nullptr};
+    };
+    Problem p0 = p;
+    size_t foot = 0;
+    for (Mat *m : ops(p0))
+        if (m && m->hi > m->lo) foot += ((m->hi - m->lo) + (m->lo % 256) + 255) / 256 * 256;
+    r->probs.push_back(p);
+    if (foot == 0) return hipSuccess;
+    const size_t sets = foot >= (size_t(512) << 20) ? 1 : std::min<size_t>(64, ((size_t(1) << 30) + foot - 1) / foot);
+    hipError_t err;
+    for (size_t k = 1; k < sets; ++k) {
+        void *buf = nullptr;
+        if ((err = hipMalloc(&buf, foot)) != hipSuccess) return err;
+        r->bufs.push_back(buf);
+        Problem q = p;
+        char *cur = static_cast<char *>(buf);
+        for (Mat *m : ops(q)) {
+            if (!m || m->hi == m->lo) continue;
+            const size_t span = m->hi - m->lo, head = m->lo % 256;
+            char *dst = cur + head;
+            if ((err = hipMemcpyAsync(dst, reinterpret_cast<const void *>(m->lo), span, hipMemcpyDeviceToDevice,
+                                      stream)) != hipSuccess)
+                return err;
+            const intptr_t delta = reinterpret_cast<intptr_t>(dst) - static_cast<intptr_t>(m->lo);
+            m->ptr += delta;
+            m->lo += delta;
+            m->hi += delta;
+            cur += (span + head + 255) / 256 * 256;
+        }
+        r->probs.push_back(q);
+    }
+    return hipSuccess;
+}
+
 dg_status tune_entry(const dg_view *A, const dg_view *SA, const dg_view *B, const dg_view *SB,
                      const dg_view *C, int32_t reps, dg_tune_result *out, hipStream_t stream) {
     if (!out) return DG_ERR_NULL;
@@ -668,12 +721,22 @@ dg_status tune_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
         if (e0) (void)hipEventDestroy(e0);
         return DG_ERR_HIP;
     }
-    // Average launch time of a plan over n launches (after one untimed launch).
+    RotationSets rot;
+    if (make_rotation(p, stream, &rot) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        return DG_ERR_HIP;
+    }
+    const size_t nsets = rot.probs.size();
+    size_t next = 0;   // the set the next launch uses
+    // Average launch time of a plan over n launches (after one untimed launch),
+    // each launch on the next set of operands.
     auto time_plan = [&](const Plan &pl, int n, double *us) -> dg_status {
         float ms = 0.f;
-        dg_status r = run_plan(p, pl, stream);
+        dg_status r = run_plan(rot.probs[next++ % nsets], pl, stream);
         if (r == DG_SUCCESS && hipEventRecord(e0, stream) != hipSuccess) r = DG_ERR_HIP;
-        for (int k = 0; r == DG_SUCCESS && k < n; ++k) r = run_plan(p, pl, stream);
+        for (int k = 0; r == DG_SUCCESS && k < n; ++k) r = run_plan(rot.probs[next++ % nsets], pl, stream);
         if (r == DG_SUCCESS && (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
             r = DG_ERR_HIP;
@@ -693,9 +756,10 @@ dg_status tune_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
         const int n_warm = (int)std::min(2000.0, std::max(1.0, 30e3 / std::max(us, 1.0)));
         if (st == DG_SUCCESS) st = time_plan(def, n_warm, &us);
         std::vector<double> t(cs.size(), 1e30);
+        const int n = std::max<int>(reps, (int)std::min<size_t>(nsets, 64));   // every set at least once
         for (int pass = 0; pass < 2 && st == DG_SUCCESS; ++pass)
             for (int i = 0; i < (int)cs.size() && st == DG_SUCCESS; ++i) {
-                st = time_plan(select_plan(p, d, cs[i]), reps, &us);
+                st = time_plan(select_plan(p, d, cs[i]), n, &us);
                 t[i] = std::min(t[i], us);
             }
         if (st == DG_SUCCESS) {
@@ -722,6 +786,11 @@ dg_status tune_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
         std::snprintf(out->plan, sizeof out->plan, "%s", describe(p, select_plan(p, d, cs[best]), d).c_str());
     }
     out->tune_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+    out->sets = (int32_t)nsets;
+    if (hipStreamSynchronize(stream) != hipSuccess) {   // the copies are freed next
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
     return DG_SUCCESS;
 }
 

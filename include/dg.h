@@ -239,6 +239,7 @@ typedef struct {
     double tune_ms;      /* wall time of the whole tuning call */
     int32_t candidates;  /* plans timed */
     int32_t chosen;      /* index of the chosen plan in dg_gemm_candidates' list */
+    int32_t sets;        /* operand sets the timing rotated over (1: the caller's only) */
     char plan[512];      /* description of the chosen plan (dg_gemm_plan's format) */
 } dg_tune_result;
 
@@ -261,11 +262,18 @@ dg_status dg_gemm_with_choice(const dg_view *A, const dg_view *A_scale, const dg
 
 /* Tune this problem on the current device: run the built-in plan for about
  * 30 ms (the clocks rise under sustained load), then time every candidate
- * twice, each time one untimed launch and `reps` launches between two events
- * on `stream` (reps 0: 5), keep the fastest for the problem's key (by each
- * candidate's better time), fill *result.  C is overwritten with A*B
- * (alpha 1, beta 0; its earlier contents are lost); A and B are only read.
- * Synchronizes `stream`.  Problems with M, N or K equal to 0 have nothing to
+ * twice, each time one untimed launch and max(reps, sets) launches between two
+ * events on `stream` (reps 0: 5), keep the fastest for the problem's key (by
+ * each candidate's better time), fill *result.  Successive launches run on
+ * distinct copies of the operands (at least 1 GiB of them in total, at most
+ * 64 sets; none for a problem of 512 MB or more), so that every candidate
+ * reads its operands from HBM, as in a workload, and not from the last-level
+ * cache: the ranking of plans for bandwidth-bound shapes depends on it
+ * (sheratonhq.com deep dive, section 5.3: tune on the target device with the
+ * real shape; cf-1.com article, section 5.2).  The copies are allocated with
+ * hipMalloc and freed before the call returns.  C (and its copies) is
+ * overwritten with A*B (alpha 1, beta 0; its earlier contents are lost); A and
+ * B are only read.  Synchronizes `stream`.  Problems with M, N or K equal to 0 have nothing to
  * tune (result->candidates = 0).
  * Errors: DG_ERR_NULL (result NULL), DG_ERR_INVALID_ARG (reps outside
  * 0..1000), the validation errors of dg_gemm / dg_gemm_fp8, DG_ERR_HIP. */
