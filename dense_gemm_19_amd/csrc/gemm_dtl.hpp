@@ -58,7 +58,10 @@ __device__ __forceinline__ int kmaj_off(int r, int c) { return r * KB + ((c ^ (r
 template <int EB, int CPR>
 __device__ __forceinline__ int mn_swz(int k) {
     int s;
-    if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
+    // 16-bit rows of 128 bytes (8 chunks): rows k and k + 2 (and k + 8, read by
+    // the next lane group) share a bank half; K bits 1 and 3 pick the chunk pair.
+    if (EB == 2 && CPR == 8) s = (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1;
+    else if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
     else if (CPR >= 32) s = (k & 7) | (((k >> 5) & 3) << 3);
     else if (CPR >= 16) s = (k & 7) ^ (((k >> 4) & 1) << 3);
     else s = (k & 7) ^ ((k >> 4) & 1);
@@ -68,6 +71,16 @@ template <int EB, int R>
 __device__ __forceinline__ int mnmaj_off(int k, int c) {
     constexpr int CPR = R * EB / 16;
     return k * (R * EB) + ((c ^ mn_swz<EB, CPR>(k)) << 4);
+}
+
+// FP8 row scales of a stage: lane row l (0..15) owns BM / 16 floats, i.e.
+// BM / 64 chunks of 16 bytes; the 16 segments, read together, start at
+// l * BM / 4 bytes, so lane rows 64 / BM * 16 apart would share banks.  Their
+// chunks are XOR-swizzled by this value, which differs between such rows.
+template <int BM>
+__device__ __forceinline__ int sa_swz(int l) {
+    constexpr int SC = BM / 64 > 0 ? BM / 64 : 1;   // chunks per segment
+    return (l / (16 / SC)) & (SC - 1);
 }
 
 // ------------------------------------------------------------------ HBM -> LDS
@@ -313,13 +326,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // FP8 scale sources of this thread's lane for the staging loads.  The BM
-    // row scales of a stage sit in LDS grouped by row mod 16: row r at float
-    // (r % 16) * (BM / 16) + r / 16, so that a lane finds the scales of its
-    // rows (one per 16-row block, see compute) side by side.  The loader lane
-    // filling float p fetches the row stored there.
+    // row scales of a stage sit in LDS grouped by row mod 16: lane row l = r % 16
+    // owns a segment of BM / 16 floats holding its rows' scales in block order
+    // b = r / 16, so that a lane finds the scales of its rows (one per 16-row
+    // block, see compute) side by side.  The segment's 16-byte chunks are
+    // XOR-swizzled by sa_swz(l) so that the 16 segments read together fall on
+    // distinct banks.  The loader lane filling float p fetches the row stored
+    // there.
     const int NBLK = (p.N + 127) >> 7;
     const int sa_pos = 64 * (wave % (F8 ? BM / 64 : 1)) + lane;
-    const int sa_row = min(m0 + (sa_pos % (BM / 16)) * 16 + sa_pos / (BM / 16), p.M - 1);
+    const int sa_l = sa_pos / (BM / 16), sa_in = sa_pos % (BM / 16);
+    const int sa_b = (((sa_in >> 2) ^ sa_swz<BM>(sa_l)) << 2) | (sa_in & 3);
+    const int sa_row = min(m0 + sa_b * 16 + sa_l, p.M - 1);
     const int sb_blk = min((n0 >> 7) + lane, NBLK - 1);
 
     // Source addresses are computed once; each tile only adds a uniform K offset.
@@ -352,19 +370,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             // This lane's rows are wm * WTM + 16 i + lane % 16 (the products are
             // formed transposed, see mma), so it needs one row scale per 16-row
             // block: TM floats side by side in the stage's scale layout.
-            const float *lsa = reinterpret_cast<const float *>(la + SA_OFF) + (lane & 15) * (BM / 16) + wm * TM;
+            const float *lsa = reinterpret_cast<const float *>(la + SA_OFF) + (lane & 15) * (BM / 16);
             const float sb = reinterpret_cast<const float *>(la + SB_OFF)[(wn * WTN) >> 7];
             float sc[TM];
             if constexpr (TM % 4 == 0) {
 #pragma unroll
                 for (int q = 0; q < TM; q += 4) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(lsa + q);
+                    const int chunk = ((wm * TM + q) >> 2) ^ sa_swz<BM>(lane & 15);
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(lsa + 4 * chunk);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sc[q + e] = v[e] * sb;
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < TM; ++q) sc[q] = lsa[q] * sb;
+                for (int q = 0; q < TM; ++q) {
+                    const int b = wm * TM + q;
+                    sc[q] = lsa[4 * ((b >> 2) ^ sa_swz<BM>(lane & 15)) + (b & 3)] * sb;
+                }
             }
             i32x8 fb[TN];
 #pragma unroll
