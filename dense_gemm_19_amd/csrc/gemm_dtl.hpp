@@ -397,8 +397,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
             // t + 1 .. t + PL are issued, so the vector ALUs work while the matrix
             // core does, and a block's sums are complete when they are read
             // (measured on FP8 4096 x 7168 x 4096: lag 1 147.5 us, 2 130.8 us,
-            // 3 to 6 about 127 us).
-            constexpr int PL = 4;   // promotion lag, in blocks
+            // 3 to 6 about 127 us).  With A column-major the transposed A reads
+            // need more registers, and a lag of 4 would spill: 2 there.
+            constexpr int PL = AMODE == MNMAJ ? 2 : 4;   // promotion lag, in blocks
             // Each step is fenced (sched_barrier) so that the compiler keeps the
             // order written here: the matrix instruction of block t, then the
             // promotion of block t - PL, whose sums are complete by then; left
