@@ -61,7 +61,10 @@ __device__ __forceinline__ int kmaj_off(int r, int c) { return r * KBYTES + ((c 
 template <int EB, int CPR>
 __device__ __forceinline__ int mn_swz(int k) {
     int s;
-    if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
+    // 16-bit rows of 128 bytes (8 chunks): rows k and k + 2 (and k + 8, read by
+    // the next lane group) share a bank half; K bits 1 and 3 pick the chunk pair.
+    if (EB == 2 && CPR == 8) s = (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1;
+    else if (EB == 2) s = ((k & 3) << 1) | (((k >> 3) & 3) << 3);
     else s = (k & 7) | (((k >> 5) & 3) << 3);
     return s & (CPR - 1);
 }
