@@ -44,7 +44,9 @@ The JSON line also carries:
                 its candidate plans, timed again over the rotated buffers,
                 with the tuning time and the calls that pay it back), and
                 moe8: the 8 MoE expert GEMMs [1,512] x [512,4096] in one
-                dg_gemm_grouped call, against the same GEMMs as 8 dg_gemm calls.
+                dg_gemm_grouped call, against the same GEMMs as 8 dg_gemm calls;
+                moe8_prefill: the same with 64 tokens per expert ([64,512] x
+                [512,4096] each, the grouped matrix-core launch).
 """
 from __future__ import annotations
 
@@ -212,20 +214,23 @@ def time_quant(dg, name, trials=5):
             "path": "quant", "algorithmic_bytes": nbytes}
 
 
-def time_grouped(dg, trials=5):
-    """The MoE experts (8 x [1,512] x [512,4096], one token row shared): one
-    dg_gemm_grouped call per step against the same 8 GEMMs as 8 dg_gemm calls,
-    both over rotated buffer sets."""
-    import ctypes
+def time_grouped(dg, name="moe8", trials=5):
+    """MoE experts through dg_gemm_grouped, one call per step, against the same
+    8 GEMMs as 8 dg_gemm calls, both over rotated buffer sets.  moe8: decode,
+    8 x [1,512] x [512,4096] with one token row shared (the grouped streaming
+    kernel); moe8_prefill: 64 tokens per expert, 8 x [64,512] x [512,4096],
+    each expert its own token block (the grouped matrix-core launch)."""
     import torch
     import synth
-    experts = synth.moe_experts()
+    shared = name == "moe8"
+    experts = synth.moe_experts() if shared else synth.moe_experts(M=64, seed=109, shared_x=False)
     E = len(experts)
     d0 = [c.to("cuda:0") for c in experts]
     x = d0[0].A
-    per = sum(storage_bytes(c) for c in d0) - (E - 1) * x.untyped_storage().nbytes()
+    per = sum(storage_bytes(c) for c in d0) - ((E - 1) * x.untyped_storage().nbytes() if shared else 0)
     P = max(2, -(-CACHE_DEFEAT_BYTES // per))
-    sets = [d0] + [[synth.Case(c.name, x, clone_view(c.B), clone_view(c.C)) for c in d0] for _ in range(P - 1)]
+    sets = [d0] + [[synth.Case(c.name, x if shared else clone_view(c.A), clone_view(c.B), clone_view(c.C))
+                    for c in d0] for _ in range(P - 1)]
     stream = torch.cuda.current_stream().cuda_stream
     L = dg.lib()
 
@@ -242,7 +247,8 @@ def time_grouped(dg, trials=5):
 
     grouped = [Grouped(cs) for cs in sets]
     separate = [Call(dg, c, stream) for cs in sets for c in cs]
-    nbytes = sum(algorithmic(c)[0] for c in experts) - (E - 1) * algorithmic_a_bytes(experts[0])
+    nbytes = sum(algorithmic(c)[0] for c in experts) - ((E - 1) * algorithmic_a_bytes(experts[0]) if shared else 0)
+    flops = sum(2.0 * c.mnk[0] * c.mnk[1] * c.mnk[2] for c in experts)
 
     def timed(calls, per_step):
         reps = 200
@@ -264,11 +270,14 @@ def time_grouped(dg, trials=5):
     plan = dg.grouped_plan([c.A for c in d0], [c.B for c in d0], [c.C for c in d0])
     del sets, grouped, separate, d0
     torch.cuda.empty_cache()
+    M = experts[0].mnk[0]
     return {"us": round(tg * 1e6, 3), "us_min": round(tg_min * 1e6, 3), "buffer_sets": P,
+            "tflops": round(flops / tg / 1e12, 2),
             "gbs": round(nbytes / tg / 1e9, 1), "frac_hbm_peak": round(nbytes / tg / 1e9 / HBM_PEAK_GBS, 4),
             "separate_us": round(ts_ * 1e6, 3), "separate_gbs": round(nbytes / ts_ / 1e9, 1),
-            "speedup_vs_separate": round(ts_ / tg, 3), "dtype": "bf16", "mnk": [1, 4096, 512],
-            "experts": E, "path": "skinny grouped", "plan": plan, "algorithmic_bytes": nbytes}
+            "speedup_vs_separate": round(ts_ / tg, 3), "dtype": "bf16", "mnk": [M, 4096, 512],
+            "experts": E, "path": "skinny grouped" if M <= 8 else "matrix-core grouped", "plan": plan,
+            "algorithmic_bytes": nbytes}
 
 
 def algorithmic_a_bytes(case):
@@ -501,7 +510,7 @@ def main():
                     help="other workloads to time: all, none, or a comma list of "
                          "c1,c3,c4,c5_128,c5_4096,c5_tail (GEMMs), <config>_gelu (the same GEMM with a "
                          "fused bias + GELU epilogue), q_a,q_b (the FP8 quantizer) and moe8 (8 MoE "
-                         "expert GEMMs in one grouped call)")
+                         "expert GEMMs in one grouped call; moe8_prefill: the same with 64 tokens per expert)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -608,10 +617,10 @@ def main():
     others = {}
     names = [] if args.configs == "none" else (
         ["c1", "c3", "c4", "c5_128", "c5_4096", "c5_tail", "q_a", "q_b", "c2a_gelu", "c4_gelu", "c5_4096_gelu",
-         "moe8"]
+         "moe8", "moe8_prefill"]
         if args.configs == "all" else args.configs.split(","))
     for n in names:
-        others[n] = (time_quant(dg, n) if n in QUANT_CONFIGS else time_grouped(dg) if n == "moe8"
+        others[n] = (time_quant(dg, n) if n in QUANT_CONFIGS else time_grouped(dg, n) if n.startswith("moe8")
                      else time_config(dg, n, tune=not args.no_tune and not n.endswith("_gelu")))
         log(n, json.dumps(others[n]))
     # fused epilogue: its cost over the plain GEMM of the same operands, and the

@@ -268,6 +268,28 @@ struct Scratch {
     int *counters = nullptr;
 };
 
+// The matrix-core kernels' arguments for problem p under plan pl.
+MfmaArgs make_mfma_args(const Problem &p, const Plan &pl, const Scratch &sc) {
+    MfmaArgs a;
+    a.a = Operand{p.A.ptr, pl.a.r_stride, pl.a.k_stride, pl.a.vec ? 1 : 0};
+    a.b = Operand{p.B.ptr, pl.b.r_stride, pl.b.k_stride, pl.b.vec ? 1 : 0};
+    a.sa = p.fp8 ? reinterpret_cast<const float *>(p.SA.ptr) : nullptr;
+    a.sa_rs = p.SA.rs; a.sa_cs = p.SA.cs;
+    a.sb = p.fp8 ? reinterpret_cast<const float *>(p.SB.ptr) : nullptr;
+    a.sb_rs = p.SB.rs; a.sb_cs = p.SB.cs;
+    a.epi = make_epi(p);
+    a.ws = sc.ws;
+    a.counters = sc.counters;
+    a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+    a.tiles_m = pl.tiles_m; a.tiles_n = pl.tiles_n;
+    a.ktiles = pl.ktiles;
+    a.kt_per_split = pl.kt_per_split;
+    a.splits = pl.splits;
+    a.group_m = pl.group_m;
+    a.dp_tiles = pl.dp_tiles;
+    return a;
+}
+
 // Enqueue the kernels of a plan whose scratch the caller provides.
 dg_status launch_plan(const Problem &p, const Plan &pl, const Scratch &sc, hipStream_t stream) {
     const Epilogue epi = make_epi(p);
@@ -294,23 +316,7 @@ dg_status launch_plan(const Problem &p, const Plan &pl, const Scratch &sc, hipSt
         a.kc = pl.sk_kc;
         e = launch_skinny(pl.sk_kind, pl.sk_mmax, a, pl.sk_grid_x, pl.sk_waves, stream);
     } else {
-        MfmaArgs a;
-        a.a = Operand{p.A.ptr, pl.a.r_stride, pl.a.k_stride, pl.a.vec ? 1 : 0};
-        a.b = Operand{p.B.ptr, pl.b.r_stride, pl.b.k_stride, pl.b.vec ? 1 : 0};
-        a.sa = p.fp8 ? reinterpret_cast<const float *>(p.SA.ptr) : nullptr;
-        a.sa_rs = p.SA.rs; a.sa_cs = p.SA.cs;
-        a.sb = p.fp8 ? reinterpret_cast<const float *>(p.SB.ptr) : nullptr;
-        a.sb_rs = p.SB.rs; a.sb_cs = p.SB.cs;
-        a.epi = epi;
-        a.ws = ws;
-        a.counters = counters;
-        a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
-        a.tiles_m = pl.tiles_m; a.tiles_n = pl.tiles_n;
-        a.ktiles = pl.ktiles;
-        a.kt_per_split = pl.kt_per_split;
-        a.splits = pl.splits;
-        a.group_m = pl.group_m;
-        a.dp_tiles = pl.dp_tiles;
+        const MfmaArgs a = make_mfma_args(p, pl, Scratch{ws, counters});
         e = pl.dtl ? launch_mfma_dtl(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, a, stream)
                    : launch_mfma(p.in_kind, pl.tile, pl.a.mode, pl.b.mode, pl.slow, a, stream);
     }
@@ -406,8 +412,18 @@ struct GroupBatch {
     size_t ws_floats = 0, counters = 0;
 };
 
+// Groups run together by the direct-to-LDS matrix-core kernel: one tile
+// configuration (input type, tile, operand storage modes), no K split.
+struct MfmaBatch {
+    int in_kind = 0, tile = 0, a_mode = 0, b_mode = 0;
+    std::vector<int> groups;
+    std::vector<Plan> plans;
+    int units = 0;
+};
+
 struct GroupedPlan {
     std::vector<GroupBatch> batches;
+    std::vector<MfmaBatch> mfma;
     std::vector<int> solo;           // groups launched one by one (empty ones excluded)
 };
 
@@ -415,7 +431,7 @@ int64_t slabs_of(const Problem &p) { return cdiv(p.N, SKINNY_BN_COLS); }
 
 GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
     GroupedPlan gp;
-    std::vector<int> cls[4];
+    std::vector<int> cls[4], rest;
     for (int g = 0; g < (int)ps.size(); ++g) {
         const Plan pl = cached_plan(ps[g], d);
         if (pl.path == Path::Noop) continue;
@@ -423,9 +439,57 @@ GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
             const int c = pl.sk_mmax == 1 ? 0 : pl.sk_mmax == 2 ? 1 : pl.sk_mmax == 4 ? 2 : 3;
             cls[c].push_back(g);
         } else {
-            gp.solo.push_back(g);
+            rest.push_back(g);
         }
     }
+    // The other groups: each is planned for its share of the CUs (its output
+    // area over all of theirs), whole (no K split: the grid of the batch is what
+    // fills the device); groups whose plan is then the direct-to-LDS kernel
+    // share a launch with the groups of the same tile configuration; the rest,
+    // and configurations with a single group, run alone with their own plan
+    // for the whole device.
+    double area = 0.0;
+    for (int g : rest) area += (double)ps[g].M * (double)ps[g].N;
+    std::vector<MfmaBatch> open;
+    std::vector<int> alone;
+    for (int g : rest) {
+        const Problem &p = ps[g];
+        Plan pl;
+        bool batch = false;
+        if (p.alpha != 0.0f && p.K > 0 && !p.fp8) {
+            Device share = d;
+            share.cus = (int)std::max<double>(1.0, std::floor(d.cus * (double)p.M * (double)p.N / area));
+            PlanChoice whole;
+            whole.path = 2;
+            whole.splits = 1;
+            whole.tail = 0;
+            pl = select_plan(p, share, whole);
+            batch = pl.path == Path::Mfma && pl.dtl && pl.splits == 1;
+        }
+        if (!batch) {
+            alone.push_back(g);
+            continue;
+        }
+        MfmaBatch *b = nullptr;
+        for (MfmaBatch &x : open)
+            if (x.in_kind == p.in_kind && x.tile == pl.tile && x.a_mode == pl.a.mode && x.b_mode == pl.b.mode &&
+                (int)x.groups.size() < MFMA_GROUP_MAX)
+                b = &x;
+        if (!b) {
+            open.emplace_back();
+            b = &open.back();
+            b->in_kind = p.in_kind; b->tile = pl.tile; b->a_mode = pl.a.mode; b->b_mode = pl.b.mode;
+        }
+        b->groups.push_back(g);
+        b->plans.push_back(pl);
+        b->units += pl.tiles_m * pl.tiles_n;
+    }
+    for (MfmaBatch &b : open) {
+        if (b.groups.size() >= 2) gp.mfma.push_back(std::move(b));
+        else alone.push_back(b.groups[0]);
+    }
+    std::sort(alone.begin(), alone.end());
+    gp.solo = alone;
     for (int c = 0; c < 4; ++c) {
         for (size_t i0 = 0; i0 < cls[c].size(); i0 += SKINNY_GROUP_MAX) {
             GroupBatch b;
@@ -550,6 +614,22 @@ dg_status grouped_entry(int G, const dg_view *A, const dg_view *B, const dg_view
             return DG_ERR_HIP;
         }
     }
+    for (const MfmaBatch &b : gp.mfma) {
+        GroupedMfmaArgs ga;
+        std::memset(&ga, 0, sizeof ga);
+        ga.ngroups = (int)b.groups.size();
+        int unit = 0;
+        for (size_t i = 0; i < b.groups.size(); ++i) {
+            ga.g[i] = make_mfma_args(ps[b.groups[i]], b.plans[i], Scratch{});
+            ga.unit_begin[i] = unit;
+            unit += b.plans[i].tiles_m * b.plans[i].tiles_n;
+        }
+        ga.unit_begin[ga.ngroups] = unit;
+        if (launch_mfma_dtl_grouped(b.in_kind, b.tile, b.a_mode, b.b_mode, ga, unit, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return DG_ERR_HIP;
+        }
+    }
     for (size_t i = 0; i < gp.solo.size(); ++i)
         if ((st = launch_plan(ps[gp.solo[i]], solo_plans[i], Scratch{lease.ws, lease.counters}, stream)) !=
             DG_SUCCESS)
@@ -581,6 +661,12 @@ dg_status grouped_plan_entry(int G, const dg_view *A, const dg_view *B, const dg
                " lds=" + std::to_string(b.lds) + " groups=";
         for (size_t i = 0; i < b.groups.size(); ++i)
             out += (i ? "," : "") + std::to_string(b.groups[i]) + ":s" + std::to_string(b.plans[i].splits);
+    }
+    static const char *modes[] = {"KMAJ", "MNMAJ"};
+    for (const MfmaBatch &b : gp.mfma) {
+        out += " | mfma tile=" + std::to_string(mfma_tile_bm(b.tile)) + "x" + std::to_string(mfma_tile_bn(b.tile)) +
+               " a=" + modes[b.a_mode] + " b=" + modes[b.b_mode] + " units=" + std::to_string(b.units) + " groups=";
+        for (size_t i = 0; i < b.groups.size(); ++i) out += (i ? "," : "") + std::to_string(b.groups[i]);
     }
     out += " | solo=";
     for (size_t i = 0; i < gp.solo.size(); ++i) out += (i ? "," : "") + std::to_string(gp.solo[i]);

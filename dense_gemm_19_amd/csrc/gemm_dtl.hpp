@@ -273,8 +273,11 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
 // is a Stream-K-style hybrid: the pieces of the leftover tiles fill the last
 // wave of workgroup slots instead of leaving part of it idle (sheratonhq.com
 // deep dive, section 5.2, names Stream-K for balancing tails).
+// The workgroup body.  t_direct >= 0: this workgroup computes tile t_direct of
+// p whole (the grouped kernel, which maps its grid itself); otherwise the tile
+// (and K piece) follows from blockIdx.x and gridDim.x as described above.
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL>
-__global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
+__device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_direct) {
     constexpr int NW = WGM * WGN;
     // Waves 0 .. NLD-1 issue the tile loads; NLD < NW leaves the others to
     // matrix work alone (a wave stalls while it issues, the queue being full).
@@ -305,7 +308,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     // Work unit: units 0 .. dp_tiles-1 are whole tiles; later units are the S
     // pieces z of the remaining tiles, a tile's pieces consecutive.
     int t, z = 0, S = 1;
-    if (!SPLIT || (int)blockIdx.x < p.dp_tiles) {
+    if (t_direct >= 0) {
+        t = t_direct;
+    } else if (!SPLIT || (int)blockIdx.x < p.dp_tiles) {
         t = xcd_remap(blockIdx.x, SPLIT ? p.dp_tiles : (int)gridDim.x);
     } else {
         const int pc = xcd_remap(blockIdx.x - p.dp_tiles, (int)gridDim.x - p.dp_tiles);
@@ -676,6 +681,33 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL>
+__global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
+    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, SPLIT, NL>(p, -1);
+}
+
+// Several problems of one tile configuration in one grid (the experts of an
+// MoE layer with more than a few tokens each, say): the grid is mapped onto
+// the XCDs as one problem would be, then workgroup u belongs to the group g
+// with unit_begin[g] <= u < unit_begin[g + 1] and computes that group's tile
+// u - unit_begin[g] whole (no K split).
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, int NL>
+__global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl_grouped(GroupedMfmaArgs ga) {
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    int g = 0;
+    while (g + 1 < ga.ngroups && u >= ga.unit_begin[g + 1]) ++g;
+    // The group's arguments, word by word through readfirstlane: the body needs
+    // them wave-uniform (its load-to-LDS instructions take scalar bases), which
+    // the compiler cannot see through the run-time group index.
+    MfmaArgs p;
+    static_assert(sizeof(MfmaArgs) % 4 == 0, "word copy");
+    const int *src = reinterpret_cast<const int *>(&ga.g[g]);
+    int *dst = reinterpret_cast<int *>(&p);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(MfmaArgs) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, false, NL>(p, u - ga.unit_begin[g]);
+}
+
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL>
 hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
@@ -691,6 +723,20 @@ hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
         }
     }
     hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, NL>), grid, dim3(64 * WGM * WGN), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int NL = 0>
+hipError_t launch_grouped_modes(int am, int bm, const GroupedMfmaArgs &a, int units, hipStream_t s) {
+    const dim3 grid(units), block(64 * WGM * WGN);
+    if (am == KMAJ && bm == KMAJ)
+        hipLaunchKernelGGL((mfma_dtl_grouped<IN, BM, BN, WGM, WGN, NS, KMAJ, KMAJ, NL>), grid, block, 0, s, a);
+    else if (am == KMAJ && bm == MNMAJ)
+        hipLaunchKernelGGL((mfma_dtl_grouped<IN, BM, BN, WGM, WGN, NS, KMAJ, MNMAJ, NL>), grid, block, 0, s, a);
+    else if (am == MNMAJ && bm == KMAJ)
+        hipLaunchKernelGGL((mfma_dtl_grouped<IN, BM, BN, WGM, WGN, NS, MNMAJ, KMAJ, NL>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((mfma_dtl_grouped<IN, BM, BN, WGM, WGN, NS, MNMAJ, MNMAJ, NL>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -720,6 +766,19 @@ hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t
     case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
     case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);
     case T64x128: return launch_modes<IN, 64, 128, 1, 4, 6>(am, bm, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// The grouped kernel with the tile configurations of launch_tiles.
+template <int IN>
+hipError_t launch_grouped_tiles(int tile, int am, int bm, const GroupedMfmaArgs &a, int units, hipStream_t s) {
+    switch (tile) {
+    case T256x256: return launch_grouped_modes<IN, 256, 256, 2, 4, 2, 4>(am, bm, a, units, s);
+    case T128x128: return launch_grouped_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, units, s);
+    case T128x64: return launch_grouped_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, units, s);
+    case T64x64: return launch_grouped_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, units, s);
+    case T64x128: return launch_grouped_modes<IN, 64, 128, 1, 4, 6>(am, bm, a, units, s);
     }
     return hipErrorInvalidValue;
 }

@@ -8,4 +8,9 @@ hipError_t launch_mfma_dtl_f16(int tile, int a_mode, int b_mode, const MfmaArgs 
     return dtl::launch_tiles<IN_F16>(tile, a_mode, b_mode, args, stream);
 }
 
+hipError_t launch_mfma_dtl_grouped_f16(int tile, int a_mode, int b_mode, const GroupedMfmaArgs &args, int units,
+                                     hipStream_t stream) {
+    return dtl::launch_grouped_tiles<IN_F16>(tile, a_mode, b_mode, args, units, stream);
+}
+
 }  // namespace dg

@@ -112,6 +112,19 @@ struct GroupedSkinnyArgs {
 };
 static_assert(sizeof(GroupedSkinnyArgs) <= 4096, "kernel arguments are limited to 4 KB");
 
+// Grouped direct-to-LDS launch (several matrix-core GEMMs of one tile
+// configuration in one grid, e.g. MoE experts with more than a few tokens
+// each): workgroup u (after the grid's XCD mapping) belongs to the group g with
+// unit_begin[g] <= u < unit_begin[g + 1] and computes that group's tile
+// u - unit_begin[g] whole.  Passed by value (at most 4 KB of kernel arguments).
+constexpr int MFMA_GROUP_MAX = 16;
+struct GroupedMfmaArgs {
+    int ngroups;
+    int unit_begin[MFMA_GROUP_MAX + 1];
+    MfmaArgs g[MFMA_GROUP_MAX];
+};
+static_assert(sizeof(GroupedMfmaArgs) <= 4096, "kernel arguments are limited to 4 KB");
+
 struct ReduceArgs {
     const float *ws;    // [S][M][N]
     Epilogue epi;
@@ -149,6 +162,9 @@ hipError_t launch_mfma(int in_kind, int tile, int a_mode, int b_mode, int slow,
 bool mfma_dtl_tile(int tile);
 hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const MfmaArgs &args,
                            hipStream_t stream);
+// units: the sum of the groups' tile counts (unit_begin[ngroups]); FP16/BF16 only.
+hipError_t launch_mfma_dtl_grouped(int in_kind, int tile, int a_mode, int b_mode, const GroupedMfmaArgs &args,
+                                   int units, hipStream_t stream);
 hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
                          hipStream_t stream);
 // m_max: the largest M class of the groups (1, 2, 4 or 8); lds_bytes: the

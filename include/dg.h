@@ -185,10 +185,15 @@ dg_status dg_gemm_fp8_epilogue(const dg_view *A, const dg_view *A_scale, const d
  *         group's A, B or C.
  *   G == 0: nothing happens.
  * Execution: groups with M <= 8 whose B is N-contiguous with 16-byte aligned
- * rows run together in one launch per M class (1, 2, 4, 8) and per 16 groups;
- * every other group runs through its own dg_gemm plan, in order, on `stream`.
+ * rows run together in one launch per M class (1, 2, 4, 8) and per 16 groups.
+ * Every other group is planned for its share of the CUs (its M*N over the sum
+ * of theirs); those whose plan is then the matrix-core kernel with direct
+ * HBM -> LDS loads and no K split run together, one launch per tile
+ * configuration (tile size, operand storage orders) and per 16 groups, when at
+ * least two share it (the experts of an MoE layer with more than a few tokens
+ * each).  The rest run through their own dg_gemm plan, in order, on `stream`.
  * Results equal those of G separate dg_gemm calls within the dg_gemm tolerance
- * (a group's K may be split differently), and are bitwise reproducible.
+ * (a group's tile and K split may differ), and are bitwise reproducible.
  * Errors: DG_ERR_INVALID_ARG (G < 0), DG_ERR_NULL (an array is NULL with
  * G > 0), the dg_gemm error of the first invalid group, DG_ERR_DTYPE (A/B
  * dtypes differ between groups), DG_ERR_ALIAS (a C overlaps another group's

@@ -5,9 +5,11 @@ Each group's result must meet the dg_gemm bound (oracle/compare.py):
 |C - C_ref| <= 1e-4 * |alpha| * S + 4 * 2^-24 * (|alpha| * S + |beta * C_in|)
 + 0.5 * ulp_out, S = sum_k |a_ik * b_kj|.  Covered: the MoE experts of the
 pages (8 x [1,512] x [512,4096], one shared token row), every M class of the
-grouped streaming kernel, ragged N and K, groups that run alone (M > 8,
-K-contiguous or unaligned B, K = 0, alpha = 0), empty groups, more than 16
-groups (several launches), and run-to-run bitwise reproducibility.
+grouped streaming kernel, ragged N and K, groups that run alone (K-contiguous
+or unaligned B, K = 0, alpha = 0, a lone matrix-core configuration), empty
+groups, more than 16 groups (several launches), the grouped matrix-core launch
+(experts with 17-256 tokens each, two operand layouts, more than 16 groups),
+and run-to-run bitwise reproducibility.
 """
 import numpy as np
 import pytest
@@ -132,3 +134,42 @@ def test_moe_full_precision_output(dg):
     for c, C in zip(cases, got):
         ref = oracle.ref_gemm(c.A, c.B)
         assert oracle.compare(C, ref, "f32", 1e-4, literal=True).ok
+
+
+# ---------------------------------------------------------------- the grouped matrix-core launch
+
+def _prefill_experts(tokens, K=512, N=4096, seed=300, b_layout="row", dtype=BF16, out=BF16):
+    """One token block [M_e, K] and one weight [K, N] per expert (an MoE layer
+    after routing, with M_e tokens sent to expert e)."""
+    return [synth.gemm_case(M, N, K, dtype, out, seed=seed + e, b_layout=b_layout, name=f"e{e}")
+            for e, M in enumerate(tokens)]
+
+
+def test_moe_prefill_experts_in_one_launch(dg):
+    cases = _prefill_experts([64, 32, 128, 17, 64, 96, 40, 64])
+    _, text = check_grouped(dg, cases)
+    assert text.count("| mfma tile=") == 1 and "groups=0,1,2,3,4,5,6,7" in text and text.endswith("solo="), text
+
+
+def test_mfma_batches_by_configuration_and_count(dg):
+    # two B storage orders (two launches), 20 groups of one order (two launches
+    # of at most 16), a K that the direct kernel cannot take (alone), FP32 C,
+    # alpha and beta
+    cases = _prefill_experts([48] * 20, K=256, N=1024, seed=400, out=F32)
+    cases += _prefill_experts([96, 33, 70], K=384, N=640, seed=500, b_layout="col", out=F32)
+    cases += [synth.gemm_case(40, 512, 200, BF16, F32, seed=600, name="k200")]
+    for c in cases:
+        c.C.copy_(synth.to_dtype(synth.draw(synth.rng(7), tuple(c.C.shape), "normal"), F32))
+    _, text = check_grouped(dg, cases, alpha=0.75, beta=-0.5)
+    assert text.count("| mfma tile=") == 3 and "b=KMAJ" in text and "b=MNMAJ" in text, text
+    assert text.endswith("solo=23"), text
+
+
+def test_mfma_batch_f16_and_bitwise_repeat(dg):
+    cases = _prefill_experts([16, 200, 64, 129], K=1024, N=2048, seed=700, dtype=F16, out=F32)
+    a, text = run_grouped(dg, cases)
+    b, _ = run_grouped(dg, cases)
+    assert "| mfma tile=" in text, text
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    check_grouped(dg, cases)
