@@ -314,6 +314,7 @@ dg_status launch_plan(const Problem &p, const Plan &pl, const Scratch &sc, hipSt
         a.splits = pl.splits;
         a.k_per_split = pl.sk_k_per_split;
         a.kc = pl.sk_kc;
+        a.cols = pl.sk_cols;
         e = launch_skinny(pl.sk_kind, pl.sk_mmax, a, pl.sk_grid_x, pl.sk_waves, stream);
     } else {
         const MfmaArgs a = make_mfma_args(p, pl, Scratch{ws, counters});
@@ -406,6 +407,7 @@ dg_status plan_entry(const dg_view *A, const dg_view *SA, const dg_view *B, cons
 
 struct GroupBatch {
     int mclass = 1;
+    bool wide = false;               // slabs wider than SKINNY_BN_COLS (the 64-lane layout)
     std::vector<int> groups;
     std::vector<Plan> plans;
     int units = 0, lds = 0;
@@ -427,6 +429,7 @@ struct GroupedPlan {
     std::vector<int> solo;           // groups launched one by one (empty ones excluded)
 };
 
+// A group's weight in the split of the CUs: its output columns in 256-wide slabs.
 int64_t slabs_of(const Problem &p) { return cdiv(p.N, SKINNY_BN_COLS); }
 
 GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
@@ -492,8 +495,9 @@ GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
     gp.solo = alone;
     for (int c = 0; c < 4; ++c) {
         for (size_t i0 = 0; i0 < cls[c].size(); i0 += SKINNY_GROUP_MAX) {
-            GroupBatch b;
-            b.mclass = 1 << c;
+            GroupBatch bw[2];   // narrow and wide slab layouts launch separately
+            bw[0].mclass = bw[1].mclass = 1 << c;
+            bw[1].wide = true;
             const size_t i1 = std::min(cls[c].size(), i0 + SKINNY_GROUP_MAX);
             int64_t total = 0;
             for (size_t i = i0; i < i1; ++i) total += slabs_of(ps[cls[c][i]]);
@@ -502,16 +506,18 @@ GroupedPlan plan_grouped(const std::vector<Problem> &ps, const Device &d) {
                 Device share = d;   // this group's share of the CUs
                 share.cus = (int)std::max<int64_t>(1, (int64_t)d.cus * slabs_of(ps[g]) / total);
                 const Plan pl = cached_plan(ps[g], share);
+                GroupBatch &b = bw[pl.sk_cols > SKINNY_BN_COLS ? 1 : 0];
                 b.groups.push_back(g);
                 b.plans.push_back(pl);
-                b.units += (int)(slabs_of(ps[g]) * pl.splits);
-                b.lds = std::max(b.lds, skinny_bn_lds(b.mclass, pl.sk_kc));
+                b.units += pl.sk_grid_x * pl.splits;
+                b.lds = std::max(b.lds, skinny_bn_lds(b.mclass, pl.sk_kc, pl.sk_cols));
                 if (pl.splits > 1) {
                     b.ws_floats += (size_t)pl.splits * (size_t)ps[g].M * (size_t)ps[g].N;
-                    b.counters += (size_t)slabs_of(ps[g]);
+                    b.counters += (size_t)pl.sk_grid_x;
                 }
             }
-            gp.batches.push_back(std::move(b));
+            for (GroupBatch &b : bw)
+                if (!b.groups.empty()) gp.batches.push_back(std::move(b));
         }
     }
     return gp;
@@ -600,16 +606,17 @@ dg_status grouped_entry(int G, const dg_view *A, const dg_view *B, const dg_view
             a.splits = pl.splits;
             a.k_per_split = pl.sk_k_per_split;
             a.kc = pl.sk_kc;
+            a.cols = pl.sk_cols;
             if (pl.splits > 1) {
                 wofs += (size_t)pl.splits * (size_t)p.M * (size_t)p.N;
-                cofs += (size_t)slabs_of(p);
+                cofs += (size_t)pl.sk_grid_x;
             }
             ga.unit_begin[i] = unit;
-            ga.slabs[i] = (int)slabs_of(p);
+            ga.slabs[i] = pl.sk_grid_x;
             unit += ga.slabs[i] * pl.splits;
         }
         ga.unit_begin[ga.ngroups] = unit;
-        if (launch_skinny_grouped(ps[0].in_kind, b.mclass, ga, b.units, b.lds, stream) != hipSuccess) {
+        if (launch_skinny_grouped(ps[0].in_kind, b.mclass, b.wide, ga, b.units, b.lds, stream) != hipSuccess) {
             (void)hipGetLastError();
             return DG_ERR_HIP;
         }
@@ -660,7 +667,8 @@ dg_status grouped_plan_entry(int G, const dg_view *A, const dg_view *B, const dg
         out += " | batch mmax=" + std::to_string(b.mclass) + " units=" + std::to_string(b.units) +
                " lds=" + std::to_string(b.lds) + " groups=";
         for (size_t i = 0; i < b.groups.size(); ++i)
-            out += (i ? "," : "") + std::to_string(b.groups[i]) + ":s" + std::to_string(b.plans[i].splits);
+            out += (i ? "," : "") + std::to_string(b.groups[i]) + ":s" + std::to_string(b.plans[i].splits) + "c" +
+                   std::to_string(b.plans[i].sk_cols);
     }
     static const char *modes[] = {"KMAJ", "MNMAJ"};
     for (const MfmaBatch &b : gp.mfma) {

@@ -83,18 +83,25 @@ struct SkinnyArgs {
     int splits;                           // S
     int k_per_split;                      // rows of K per split (multiple of 8)
     int kc;                               // SK_BN: rows of A staged in LDS at a time
+    int cols;                             // SK_BN: columns per slab (multiple of 8, <= SKINNY_BN_WIDE_COLS)
 };
 
-// SK_BN geometry: 512 threads, 256 columns per workgroup, 128-row sweeps; the
-// A chunk kc is a multiple of the sweep.
+// SK_BN geometry: 512 threads, a slab of at most 256 columns per workgroup
+// (32 lanes per row piece), or of 264 to 512 columns (64 lanes per row piece,
+// the wide layout, for M <= SKINNY_WIDE_MMAX); the slab width is chosen per
+// problem so that the slabs times the K splits fill the CUs.  K splits and A
+// chunks are multiples of 128 rows.
 constexpr int SKINNY_BN_THREADS = 512;
 constexpr int SKINNY_BN_COLS = 256;
+constexpr int SKINNY_BN_WIDE_COLS = 512;
+constexpr int SKINNY_WIDE_MMAX = 4;
 constexpr int SKINNY_BN_SWEEP = 128;
 // LDS bytes of SK_BN: the A chunk [mmax][kc] 16-bit plus a spare 16-byte slot,
-// or the cross-wave reduction buffer [8 waves][mmax][256] FP32, whichever is
-// larger.
-inline int skinny_bn_lds(int mmax, int kc) {
-    const int a = mmax * kc * 2 + 16, r = (SKINNY_BN_THREADS / 64) * mmax * SKINNY_BN_COLS * 4;
+// or the cross-wave reduction buffer [8 waves][mmax][256 or 512] FP32,
+// whichever is larger.
+inline int skinny_bn_lds(int mmax, int kc, int cols) {
+    const int w = cols > SKINNY_BN_COLS ? SKINNY_BN_WIDE_COLS : SKINNY_BN_COLS;
+    const int a = mmax * kc * 2 + 16, r = (SKINNY_BN_THREADS / 64) * mmax * w * 4;
     return a > r ? a : r;
 }
 
@@ -167,9 +174,10 @@ hipError_t launch_mfma_dtl_grouped(int in_kind, int tile, int a_mode, int b_mode
                                    int units, hipStream_t stream);
 hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x, int waves,
                          hipStream_t stream);
-// m_max: the largest M class of the groups (1, 2, 4 or 8); lds_bytes: the
+// m_max: the largest M class of the groups (1, 2, 4 or 8); wide: the groups'
+// slabs are wider than SKINNY_BN_COLS (all or none of them); lds_bytes: the
 // largest skinny_bn_lds of the groups.
-hipError_t launch_skinny_grouped(int in_kind, int m_max, const GroupedSkinnyArgs &args, int units,
+hipError_t launch_skinny_grouped(int in_kind, int m_max, bool wide, const GroupedSkinnyArgs &args, int units,
                                  int lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &args, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs &args, hipStream_t stream);

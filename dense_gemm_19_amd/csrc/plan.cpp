@@ -16,6 +16,7 @@ struct Overrides {
     int force_path = 0;    // 0 none, 1 skinny, 2 mfma
     int force_splitk = 0;
     int force_tile = -1;
+    int skinny_cols = 0;   // SK_BN slab width (multiple of 8, at most 256)
     bool no_vec = false;
     bool no_dtl = false;
     bool no_tail_split = false;
@@ -36,6 +37,10 @@ const Overrides &overrides() {
                 std::snprintf(name, sizeof name, "%dx%d", mfma_tile_bm(t), mfma_tile_bn(t));
                 if (!std::strcmp(s, name)) r.force_tile = t;
             }
+        }
+        if (const char *s = std::getenv("DG_SKINNY_COLS")) {
+            const int v = std::atoi(s);
+            if (v > 0 && v % 8 == 0 && v <= SKINNY_BN_WIDE_COLS) r.skinny_cols = v;
         }
         if (const char *s = std::getenv("DG_NO_VEC")) r.no_vec = s[0] == '1';
         if (const char *s = std::getenv("DG_NO_DTL")) r.no_dtl = s[0] == '1';
@@ -83,29 +88,82 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
     const Mat &A = p.A, &B = p.B;
     const int mmax = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
     const bool no_vec = overrides().no_vec;
-    // B N-contiguous: stream 512-byte row pieces of B, 256 columns per workgroup.
+    // B N-contiguous: stream row pieces of B, a slab of at most 256 columns per
+    // workgroup.
     if (!no_vec && B.cols_contig() && B.cs == B.esize && B.align_ptr >= 16 && (p.K <= 1 || B.align_rs >= 16)) {
         pl.sk_kind = SK_BN;
-        pl.sk_grid_x = (int)cdiv(p.N, SKINNY_BN_COLS);
-        // Split K so that the grid fills the CUs without overfilling them: at
-        // most one workgroup per CU (a CU holding two would stream and multiply
-        // twice as much as the others and set the pace).  The splits are whole
-        // sweeps of as nearly equal length as the count allows (the last
-        // workgroup of a slab sums the partials), with at least two sweeps each.
+        // Slabs x K splits should fill the CUs once: a CU streams at a bounded
+        // rate, so an idle CU is lost bandwidth, and a CU holding two workgroups
+        // streams twice as much as the others and sets the pace.  For each
+        // split count S (whole sweeps of as nearly equal length as S allows, at
+        // least two each) the slab is the narrowest multiple of 8 columns (at
+        // most 256, or 512 in the wide layout for M <= SKINNY_WIDE_MMAX, and at
+        // least 64, i.e. 128-byte lines, where N allows) that keeps slabs x S
+        // within the CUs.  The score is the CUs kept busy, discounted for
+        // unequal splits and for the bytes of 128-byte lines a row's slabs
+        // touch beyond the row itself (a slab edge inside a line makes two
+        // workgroups fetch that line).  Among scores within 3% of the best the
+        // widest slab wins, then the fewest splits: measured on x.W1 (BF16,
+        // N = 14336, K = 4096, 256 CUs), 512-byte row pieces on 224 workgroups
+        // took 21.3 us, 448-byte pieces on 256 workgroups 23.8 us, 256-byte
+        // pieces 25.7 us and 128-byte pieces 34.6 us.
         const int64_t sweep = SKINNY_BN_SWEEP;
         const int64_t sweeps = cdiv(std::max<int64_t>(p.K, 1), sweep);
-        int64_t S = std::max<int64_t>(1, std::min<int64_t>(d.cus / pl.sk_grid_x, sweeps / 2));
-        if (overrides().force_splitk > 0) S = std::min<int64_t>(overrides().force_splitk, sweeps);
-        if (c.splits > 0) S = std::min<int64_t>(c.splits, sweeps);
-        // splits and LDS chunks are whole sweeps (only the last sweep of K is partial)
-        const int64_t kps = cdiv(sweeps, S) * sweep;
+        const int64_t maxcols = mmax <= SKINNY_WIDE_MMAX ? SKINNY_BN_WIDE_COLS : SKINNY_BN_COLS;
+        auto geometry = [&](int64_t S, int64_t &kps, int64_t &cols, int64_t &slabs) {
+            kps = cdiv(sweeps, S) * sweep;
+            S = cdiv(std::max<int64_t>(p.K, 1), kps);
+            const int64_t target = std::max<int64_t>(1, d.cus / S);
+            const int64_t lo = std::min<int64_t>(64, cdiv(std::max<int64_t>(p.N, 1), 8) * 8);
+            cols = std::min<int64_t>(maxcols, std::max<int64_t>(lo, cdiv(cdiv(p.N, target), 8) * 8));
+            if (overrides().skinny_cols > 0) cols = std::min<int64_t>(maxcols, overrides().skinny_cols);
+            slabs = cdiv(p.N, cols);
+            return S;
+        };
+        // bytes of a row of B over the bytes of the 128-byte lines its slabs
+        // fetch (rows assumed to start on a line)
+        auto line_eff = [&](int64_t cols, int64_t slabs) {
+            const int64_t es = B.esize, row = p.N * es;
+            int64_t lines = 0;
+            for (int64_t sl = 0; sl < slabs; ++sl) {
+                const int64_t b0 = sl * cols * es, b1 = std::min(row, (sl + 1) * cols * es);
+                lines += (b1 - 1) / 128 - b0 / 128 + 1;
+            }
+            return (double)row / (double)(lines * 128);
+        };
+        int64_t S = 1;
+        const int64_t forced = c.splits > 0 ? c.splits : overrides().force_splitk;
+        if (forced > 0) {
+            S = std::min<int64_t>(forced, sweeps);
+        } else {
+            const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(sweeps / 2, d.cus));
+            struct Opt { int64_t S, cols; double score; };
+            std::vector<Opt> opts;
+            double best = 0.0;
+            for (int64_t s = 1; s <= smax; ++s) {
+                int64_t kps, cols, slabs;
+                if (geometry(s, kps, cols, slabs) != s) continue;   // the rounding gives another count
+                const double units = (double)(slabs * s);
+                const double busy = units / std::max<double>(1.0, std::ceil(units / d.cus));   // per wave of CUs
+                const double score = busy * ((double)sweeps / (double)(s * (kps / sweep))) * line_eff(cols, slabs);
+                opts.push_back({s, cols, score});
+                best = std::max(best, score);
+            }
+            int64_t wide_cols = 0;
+            for (const Opt &o : opts)
+                if (o.score >= 0.97 * best && o.cols > wide_cols) { S = o.S; wide_cols = o.cols; }
+        }
+        int64_t kps, cols, slabs;
+        geometry(S, kps, cols, slabs);
+        pl.sk_grid_x = (int)slabs;
+        pl.sk_cols = (int)cols;
         pl.sk_k_per_split = (int)kps;
         pl.splits = (int)cdiv(std::max<int64_t>(p.K, 1), kps);
         pl.sk_mmax = mmax;
         // A chunk in LDS: a multiple of the sweep, at most 32 KB
         const int64_t kc_max = std::max<int64_t>(sweep, (16384 / mmax) / sweep * sweep);
         pl.sk_kc = (int)std::min<int64_t>(cdiv(kps, sweep) * sweep, kc_max);
-        pl.lds_bytes = skinny_bn_lds(mmax, pl.sk_kc);
+        pl.lds_bytes = skinny_bn_lds(mmax, pl.sk_kc, pl.sk_cols);
         pl.counters = pl.splits > 1 ? pl.sk_grid_x : 0;
         // A staged with 16-byte loads: K-contiguous 16-byte-aligned rows, and K a
         // multiple of 8 so that no piece crosses the end of a row
@@ -529,6 +587,7 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
         add(" path=skinny kind=%s mmax=%d grid=%dx%d k_per_split=%d splits=%d kc=%d waves=%d a_vec=%d lds=%d",
             pl.sk_kind == SK_BN ? "BN" : "BK", pl.sk_mmax, pl.sk_grid_x, pl.splits, pl.sk_k_per_split,
             pl.splits, pl.sk_kc, pl.sk_kind == SK_BN ? SKINNY_BN_THREADS / 64 : pl.sk_waves, pl.sk_a_vec, pl.lds_bytes);
+        if (pl.sk_kind == SK_BN) add(" cols=%d", pl.sk_cols);
         break;
     case Path::Mfma:
         add(" path=mfma tile=%dx%d a=%s b=%s vec=%d/%d slow=%d dtl=%d tiles=%dx%d ktiles=%d splits=%d "

@@ -61,6 +61,7 @@ struct Plan {
     // streaming path
     int sk_kind = SK_BN, sk_mmax = 1, sk_grid_x = 0, sk_k_per_split = 0, sk_a_vec = 0;
     int sk_kc = 0;            // SK_BN: A rows staged in LDS per chunk
+    int sk_cols = 0;          // SK_BN: columns per slab (multiple of 8, at most SKINNY_BN_WIDE_COLS)
     int sk_waves = 1;         // SK_BK: waves (columns) per workgroup
     // both
     int splits = 1;

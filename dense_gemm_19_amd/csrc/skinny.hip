@@ -11,11 +11,15 @@
 // article, section 4.5), so results are reproducible.
 //
 // SK_BN: B is N-contiguous (row-major [K][N], e.g. W1).  A workgroup of 8 waves
-//   owns a slab of 256 columns (512 bytes of every row of B) and one split of
-//   K.  Lane (r, c) of a wave, r = lane/32, c = lane%32, owns columns
-//   8c..8c+7 of the slab and, in each 128-row sweep, the 8 consecutive rows
-//   8*(2*wave + r) + u, u < 8: every load instruction of a wave reads two whole
-//   512-byte row pieces, and the A values a lane needs are 16-byte LDS reads.
+//   owns a slab of p.cols <= 256 columns (2 * p.cols bytes of every row of B)
+//   and one split of K.  Lane (r, c) of a wave, r = lane/32, c = lane%32, owns
+//   columns 8c..8c+7 of the slab (lanes with 8c >= p.cols load nothing of B)
+//   and, in each 128-row sweep, the 8 consecutive rows 8*(2*wave + r) + u,
+//   u < 8: every load instruction of a wave reads two whole row pieces of the
+//   slab, and the A values a lane needs are 16-byte LDS reads.  The slab width
+//   is planned so that slabs x K splits fill the CUs once (x.W1, N = 14336:
+//   64 slabs of 224 columns x 4 splits = 256 workgroups; 256-column slabs
+//   would leave 32 of 256 CUs idle, and each CU streams at a bounded rate).
 //   A's K slice is staged in LDS as 16-bit values [m][k], with the first
 //   sweep's loads of B already in flight.  The two row groups of a wave are
 //   summed with a shuffle and the 8 waves through LDS, always in the same
@@ -68,16 +72,20 @@ __device__ __attribute__((aligned(16))) const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 constexpr int BN_NT = SKINNY_BN_THREADS;        // 8 waves
 constexpr int BN_WAVES = BN_NT / 64;
-constexpr int BN_W = 32;                        // lanes per row: 512 contiguous bytes of a row
-constexpr int BN_R = 64 / BN_W;                 // rows per load instruction of a wave
-constexpr int BN_COLS = SKINNY_BN_COLS;         // columns per workgroup (BN_W lanes x 8)
 constexpr int BN_U = 8;                         // consecutive rows per lane per sweep
-constexpr int BN_SWEEP = BN_WAVES * BN_R * BN_U;
-static_assert(BN_COLS == BN_W * 8 && BN_SWEEP == SKINNY_BN_SWEEP, "shared with the planner");
+static_assert(SKINNY_BN_SWEEP % (BN_WAVES * BN_U) == 0, "splits and chunks are whole sweeps");
 
 // One workgroup's share of an SK_BN problem: column slab `slab`, K split `z`.
-template <int MMAX, int IN>
+// W lanes cover a row piece of a slab (W * 8 columns at most): W = 32, two row
+// pieces of up to 512 bytes per load instruction of a wave; W = 64, one piece
+// of up to 1 KB.
+template <int MMAX, int IN, int W>
 __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int slab, const int z) {
+    constexpr int BN_W = W;                     // lanes per row
+    constexpr int BN_R = 64 / BN_W;             // rows per load instruction of a wave
+    constexpr int BN_COLS = BN_W * 8;           // most columns per workgroup
+    constexpr int BN_SWEEP = BN_WAVES * BN_R * BN_U;
+    static_assert(SKINNY_BN_SWEEP % BN_SWEEP == 0, "planner sweeps are whole kernel sweeps");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // LDS: A chunk as 16-bit values [MMAX][kc] (kc a multiple of BN_SWEEP), later
     // reused for the cross-wave reduction red[wave][m][BN_COLS].
@@ -86,12 +94,21 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
     __shared__ int is_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % BN_W, r = lane / BN_W;
-    const int n0 = slab * BN_COLS + c * 8;
+    const int cols = p.cols;
+    const int n0 = slab * cols + c * 8;
     const int kb = z * p.k_per_split;
     const int ke = min(kb + p.k_per_split, p.K);
-    // every column of the slab exists: the vector path (uniform over the workgroup)
-    const bool slab_full = (slab + 1) * BN_COLS <= p.N;
-    const char *bcol = p.B + (int64_t)n0 * p.b_cs;
+    // A lane whose 8 columns all lie in the slab and in the matrix streams
+    // them with 16-byte loads.  The other lanes run the same code on the
+    // 16-byte zero block (row stride 0), so the loop stays uniform: lanes past
+    // the slab's width or past N contribute nothing, and the one lane whose
+    // columns straddle N (a ragged last slab) adds its columns with element
+    // loads after each chunk's sweeps.
+    const bool in_slab = c * 8 < cols;
+    const bool vec = in_slab && n0 + 8 <= p.N;
+    const bool straddle = in_slab && n0 < p.N && n0 + 8 > p.N;
+    const char *bcol = vec ? p.B + (int64_t)n0 * p.b_cs : reinterpret_cast<const char *>(&g_zero16);
+    const int64_t brs = vec ? p.b_rs : 0;
 
     float acc[MMAX][8];
 #pragma unroll
@@ -123,13 +140,13 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
     for (int c0 = kb; c0 < ke; c0 += p.kc) {
         const int c1 = min(c0 + p.kc, ke);
         const int clen = c1 - c0;
-        const int nfull = slab_full ? clen / BN_SWEEP : 0;   // whole sweeps of this chunk
+        const int nfull = clen / BN_SWEEP;   // whole sweeps of this chunk
         // The first sweep's loads of B go out before A is staged.  They are
         // issued unconditionally (from the 16-byte zero block when there is no
         // whole sweep), so the wait for A below is exactly "all but these 8".
         const bool first = nfull > 0;
-        const char *fb = first ? bcol + (int64_t)(c0 + lrow) * p.b_rs : reinterpret_cast<const char *>(&g_zero16);
-        const int64_t fs = first ? p.b_rs : 0;
+        const char *fb = first ? bcol + (int64_t)(c0 + lrow) * brs : reinterpret_cast<const char *>(&g_zero16);
+        const int64_t fs = first ? brs : 0;
         u32x4 v[BN_U];
 
         // Stage A[0..MMAX)[c0..c1) in LDS (rows >= M and k >= c1 as zeros).  With
@@ -181,24 +198,24 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
         for (int s = 0; s < nfull; ++s) {
             const int k = s * BN_SWEEP + lrow;
             if (s > 0) {
-                const char *q = bcol + (int64_t)(c0 + k) * p.b_rs;
+                const char *q = bcol + (int64_t)(c0 + k) * brs;
 #pragma unroll
                 for (int u = 0; u < BN_U; ++u)
-                    v[u] = __builtin_nontemporal_load((const gu32x4 *)(q + u * p.b_rs));
+                    v[u] = __builtin_nontemporal_load((const gu32x4 *)(q + u * brs));
             }
             fma_sweep(v, k);
         }
         // the partial last sweep of K (full slab), with per-row guards
-        if (slab_full && nfull * BN_SWEEP < clen) {
+        if (nfull * BN_SWEEP < clen) {
             const int k = nfull * BN_SWEEP + lrow;
 #pragma unroll
             for (int u = 0; u < BN_U; ++u) {
                 v[u] = u32x4{0u, 0u, 0u, 0u};
-                if (k + u < clen) v[u] = *(const gu32x4 *)(bcol + (int64_t)(c0 + k + u) * p.b_rs);
+                if (k + u < clen) v[u] = *(const gu32x4 *)(bcol + (int64_t)(c0 + k + u) * brs);
             }
             fma_sweep(v, k);
         }
-        if (!slab_full) {
+        if (straddle) {
             // ragged right edge: element loads; columns beyond N contribute nothing
             for (int k = lrow; k < clen; k += BN_SWEEP) {
                 for (int u = 0; u < BN_U && k + u < clen; ++u) {
@@ -217,12 +234,13 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
         }
     }
 
-    // Sum the two row groups of a wave (lanes c and c + 32), then the 8 waves
-    // through LDS: red[wave][m][BN_COLS], always in the same order.
+    // Sum the two row groups of a wave (W = 32: lanes c and c + 32), then the 8
+    // waves through LDS: red[wave][m][BN_COLS], always in the same order.
 #pragma unroll
     for (int m = 0; m < MMAX; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[m][j] += __shfl_xor(acc[m][j], 32);
+        for (int j = 0; j < 8; ++j)
+            if (BN_R == 2) acc[m][j] += __shfl_xor(acc[m][j], 32);
     __syncthreads();   // the A chunk is no longer needed
     if (lane < BN_W) {
 #pragma unroll
@@ -231,9 +249,9 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
             for (int j = 0; j < 8; ++j) red[(wave * MMAX + m) * BN_COLS + lane * 8 + j] = acc[m][j];
     }
     __syncthreads();
-    for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
-        const int m = t / BN_COLS, col = t - m * BN_COLS;
-        const int n = slab * BN_COLS + col;
+    for (int t = tid; t < MMAX * cols; t += BN_NT) {
+        const int m = t / cols, col = t - m * cols;
+        const int n = slab * cols + col;
         if (m < p.M && n < p.N) {
             float s = red[m * BN_COLS + col];
 #pragma unroll
@@ -260,9 +278,9 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
     __syncthreads();
     if (!is_last) return;
     const int64_t plane = (int64_t)p.M * p.N;
-    for (int t = tid; t < MMAX * BN_COLS; t += BN_NT) {
-        const int m = t / BN_COLS, col = t - m * BN_COLS;
-        const int n = slab * BN_COLS + col;
+    for (int t = tid; t < MMAX * cols; t += BN_NT) {
+        const int m = t / cols, col = t - m * cols;
+        const int n = slab * cols + col;
         if (m < p.M && n < p.N) {
             float *w = p.ws + (int64_t)m * p.N + n;
             const float s = sum_partials(p.splits, [&](int q) {
@@ -274,21 +292,21 @@ __device__ __forceinline__ void skinny_bn_body(const SkinnyArgs &p, const int sl
     if (tid == 0) __hip_atomic_store(p.counters + slab, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MMAX, int IN>
+template <int MMAX, int IN, int W>
 __global__ void __launch_bounds__(BN_NT) skinny_bn(SkinnyArgs p) {
-    skinny_bn_body<MMAX, IN>(p, blockIdx.x, blockIdx.y);
+    skinny_bn_body<MMAX, IN, W>(p, blockIdx.x, blockIdx.y);
 }
 
 // Several SK_BN problems in one grid (the experts of an MoE layer, say): the
 // group of this workgroup is found by a scan of at most SKINNY_GROUP_MAX
 // uniform values, then the workgroup runs exactly what skinny_bn would.
-template <int MMAX, int IN>
+template <int MMAX, int IN, int W>
 __global__ void __launch_bounds__(BN_NT) skinny_bn_grouped(GroupedSkinnyArgs p) {
     const int u = blockIdx.x;
     int g = 0;
     while (g + 1 < p.ngroups && u >= p.unit_begin[g + 1]) ++g;
     const int local = u - p.unit_begin[g];
-    skinny_bn_body<MMAX, IN>(p.g[g], local % p.slabs[g], local / p.slabs[g]);
+    skinny_bn_body<MMAX, IN, W>(p.g[g], local % p.slabs[g], local / p.slabs[g]);
 }
 
 // ------------------------------------------------------------------ SK_BK
@@ -369,21 +387,28 @@ __global__ void __launch_bounds__(256) skinny_bk(SkinnyArgs p) {
     }
 }
 
+template <int MMAX, int IN, int W>
+hipError_t launch_bn(const SkinnyArgs &a, dim3 grid, int lds, hipStream_t s) {
+    if (lds > 48 * 1024) {
+        static int attr = 0;   // benign race: setting the attribute twice is harmless
+        if (lds > attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn<MMAX, IN, W>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+            attr = lds;
+        }
+    }
+    hipLaunchKernelGGL((skinny_bn<MMAX, IN, W>), grid, dim3(BN_NT), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int MMAX, int IN>
 hipError_t launch_k(int kind, const SkinnyArgs &a, int grid_x, int waves, hipStream_t s) {
     dim3 grid(grid_x, a.splits);
     if (kind == SK_BN) {
-        const int lds = skinny_bn_lds(MMAX, a.kc);
-        if (lds > 48 * 1024) {
-            static int attr = 0;   // benign race: setting the attribute twice is harmless
-            if (lds > attr) {
-                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn<MMAX, IN>),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-                if (e != hipSuccess) return e;
-                attr = lds;
-            }
-        }
-        hipLaunchKernelGGL((skinny_bn<MMAX, IN>), grid, dim3(BN_NT), lds, s, a);
+        const int lds = skinny_bn_lds(MMAX, a.kc, a.cols);
+        if (a.cols > 256) return launch_bn<MMAX, IN, 64>(a, grid, lds, s);
+        return launch_bn<MMAX, IN, 32>(a, grid, lds, s);
     } else {
         hipLaunchKernelGGL((skinny_bk<MMAX, IN>), grid, dim3(64 * waves), 0, s, a);
     }
@@ -401,28 +426,33 @@ hipError_t launch_m(int kind, int m_max, const SkinnyArgs &a, int grid_x, int wa
     return hipErrorInvalidValue;
 }
 
-template <int MMAX, int IN>
-hipError_t launch_grouped_k(const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
+template <int MMAX, int IN, int W>
+hipError_t launch_grouped_w(const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
     if (lds > 48 * 1024) {
         static int attr = 0;   // benign race: setting the attribute twice is harmless
         if (lds > attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn_grouped<MMAX, IN>),
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_bn_grouped<MMAX, IN, W>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
             attr = lds;
         }
     }
-    hipLaunchKernelGGL((skinny_bn_grouped<MMAX, IN>), dim3(units), dim3(BN_NT), lds, s, a);
+    hipLaunchKernelGGL((skinny_bn_grouped<MMAX, IN, W>), dim3(units), dim3(BN_NT), lds, s, a);
     return hipGetLastError();
 }
 
+template <int MMAX, int IN>
+hipError_t launch_grouped_k(bool wide, const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
+    return wide ? launch_grouped_w<MMAX, IN, 64>(a, units, lds, s) : launch_grouped_w<MMAX, IN, 32>(a, units, lds, s);
+}
+
 template <int IN>
-hipError_t launch_grouped_m(int m_max, const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
+hipError_t launch_grouped_m(int m_max, bool wide, const GroupedSkinnyArgs &a, int units, int lds, hipStream_t s) {
     switch (m_max) {
-    case 1: return launch_grouped_k<1, IN>(a, units, lds, s);
-    case 2: return launch_grouped_k<2, IN>(a, units, lds, s);
-    case 4: return launch_grouped_k<4, IN>(a, units, lds, s);
-    case 8: return launch_grouped_k<8, IN>(a, units, lds, s);
+    case 1: return launch_grouped_k<1, IN>(wide, a, units, lds, s);
+    case 2: return launch_grouped_k<2, IN>(wide, a, units, lds, s);
+    case 4: return launch_grouped_k<4, IN>(wide, a, units, lds, s);
+    case 8: return launch_grouped_k<8, IN>(wide, a, units, lds, s);
     }
     return hipErrorInvalidValue;
 }
@@ -435,10 +465,10 @@ hipError_t launch_skinny(int kind, int m_max, const SkinnyArgs &args, int grid_x
     return launch_m<IN_F16>(kind, m_max, args, grid_x, waves, stream);
 }
 
-hipError_t launch_skinny_grouped(int in_kind, int m_max, const GroupedSkinnyArgs &args, int units,
+hipError_t launch_skinny_grouped(int in_kind, int m_max, bool wide, const GroupedSkinnyArgs &args, int units,
                                  int lds_bytes, hipStream_t stream) {
-    if (in_kind == IN_BF16) return launch_grouped_m<IN_BF16>(m_max, args, units, lds_bytes, stream);
-    return launch_grouped_m<IN_F16>(m_max, args, units, lds_bytes, stream);
+    if (in_kind == IN_BF16) return launch_grouped_m<IN_BF16>(m_max, wide, args, units, lds_bytes, stream);
+    return launch_grouped_m<IN_F16>(m_max, wide, args, units, lds_bytes, stream);
 }
 
 }  // namespace dg

@@ -79,7 +79,7 @@ def check_epi(dg, case, rows=None, want_in_plan=()):
 PATHS = [
     # (M, N, K, b_layout, a_layout, what the plan must say)
     (1, 1000, 777, "row", "row", ("path=skinny", "kind=BN", "splits=3")),
-    (2, 14336, 4096, "row", "row", ("path=skinny", "kind=BN", "splits=4")),
+    (2, 14336, 4096, "row", "row", ("path=skinny", "kind=BN", "splits=8", "cols=448")),
     (8, 64, 8, "row", "row", ("path=skinny", "kind=BN", "splits=1")),
     (3, 129, 1000, "col", "row", ("path=skinny", "kind=BK")),
     (65, 129, 255, "row", "row", ("path=mfma", "dtl=0", "splits=1")),

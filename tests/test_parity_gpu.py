@@ -241,6 +241,24 @@ def test_skinny_bn(dg, M, nk):
     check(dg, c)
 
 
+@pytest.mark.parametrize("mnk", [(1, 14003, 2048), (4, 9003, 1000), (8, 5003, 1000), (2, 1003, 4096), (3, 301, 777)],
+                         ids=lambda t: "x".join(map(str, t)))
+def test_skinny_bn_ragged_slabs(dg, mnk):
+    # N not a multiple of 8, B rows padded to a 16-byte pitch with NaN: in the
+    # last column slab one lane's 8 columns straddle N (element loads), the lanes
+    # past N and past the slab width read nothing of B, and any read of the
+    # padding would surface as NaN.  Slab widths from 64 to 440 columns, the
+    # 32-lane and the 64-lane row layouts, with and without K splits.
+    M, N, K = mnk
+    c = synth.gemm_case(M, N, K, BF16, torch.float32, seed=M + N + K, b_layout="pad", pad=(8 - N % 8) % 8 + 8)
+    kind, text = _plan_field(dg, c, "kind")
+    assert "path=skinny" in text and kind == "BN", text
+    cols = int(_plan_field(dg, c, "cols")[0])
+    assert 64 <= cols <= 512 and cols % 8 == 0, text
+    print(f"[skinny] {M}x{N}x{K} cols={cols} splits={_plan_field(dg, c, 'splits')[0]}", flush=True)
+    check(dg, c)
+
+
 @pytest.mark.parametrize("nk", [(1, 8), (128, 4096), (129, 1000), (1500, 4104), (7, 9000)],
                          ids=lambda t: f"N{t[0]}K{t[1]}")
 @pytest.mark.parametrize("M", [1, 3, 8])
