@@ -533,9 +533,16 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
         }
         return v;
     };
-    auto finish = [&](auto OUTK, auto FUSED) __attribute__((always_inline)) {
+    // C_in of this lane's elements, loaded ahead by the split path (see below)
+    // where the registers allow (at most 8 blocks: the 128 x 128 split kernel
+    // would drop from two waves per SIMD to one); cin_pre[i][j][e] belongs to
+    // element (i, j, e).  Unused otherwise.
+    constexpr bool PRE_CIN = SPLIT && TM * TN <= 8;
+    float cin_pre[PRE_CIN ? TM : 1][PRE_CIN ? TN : 1][4];
+    auto finish = [&](auto OUTK, auto FUSED, auto PRE) __attribute__((always_inline)) {
         constexpr int ok = decltype(OUTK)::value;
         constexpr bool fused = decltype(FUSED)::value;
+        constexpr bool pre = decltype(PRE)::value;
         float bias[TN][4];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -558,7 +565,12 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             // values past the edge are never stored
             const char *crow = ep.C + (int64_t)min(m, p.M - 1) * ep.c_rs;
             float cin[TN][4], out[TN][4];
-            if (ep.beta != 0.0f) {
+            if constexpr (pre) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cin[j][e] = cin_pre[PRE_CIN ? i : 0][PRE_CIN ? j : 0][e];
+            } else if (ep.beta != 0.0f) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int n = nc + 16 * j;
@@ -598,21 +610,21 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             }
         }
     };
-    auto finish_kind = [&](auto FUSED) __attribute__((always_inline)) {
-        if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{}, FUSED);
-        else if (ep.out_kind == OUT_BF16) finish(std::integral_constant<int, OUT_BF16>{}, FUSED);
-        else finish(std::integral_constant<int, OUT_F16>{}, FUSED);
+    auto finish_kind = [&](auto FUSED, auto PRE) __attribute__((always_inline)) {
+        if (ep.out_kind == OUT_F32) finish(std::integral_constant<int, OUT_F32>{}, FUSED, PRE);
+        else if (ep.out_kind == OUT_BF16) finish(std::integral_constant<int, OUT_BF16>{}, FUSED, PRE);
+        else finish(std::integral_constant<int, OUT_F16>{}, FUSED, PRE);
     };
-    auto finish_any = [&]() __attribute__((always_inline)) {
-        if (ep.plain()) finish_kind(std::false_type{});
-        else finish_kind(std::true_type{});
+    auto finish_any = [&](auto PRE) __attribute__((always_inline)) {
+        if (ep.plain()) finish_kind(std::false_type{}, PRE);
+        else finish_kind(std::true_type{}, PRE);
     };
     // Split K is a separate instantiation (SPLIT), so that the kernels without
     // it keep their registers; it exists for tiles of at most 64 accumulator
     // registers per lane (the reduction stages partials beside them).
     static_assert(!SPLIT || TM * TN <= 16, "split K only for small tiles");
     if (!SPLIT || S == 1) {
-        finish_any();
+        finish_any(std::false_type{});
         return;
     }
     // split K: publish this piece's partial tile with agent-scope stores, wait
@@ -636,6 +648,38 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             for (int e = 0; e < 4; ++e)
                 __hip_atomic_store(slot(z, i, j, e), acc[i][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
+    // With beta != 0 every piece loads its elements' C_in now, after its
+    // partials are acknowledged and before the ticket: the loads then overlap
+    // the ticket's round trip and the partial loads of the last piece, which
+    // alone uses them (one C_in round trip per 16-row block at the end
+    // otherwise).  The other pieces' loads mostly hit the L2 of their XCD.
+    auto preload = [&](auto OUTK) __attribute__((always_inline)) {
+        constexpr int ok = decltype(OUTK)::value;
+        if constexpr (PRE_CIN) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const char *crow = ep.C + (int64_t)min(mr + 16 * i, p.M - 1) * ep.c_rs;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = nc + 16 * j;
+                if (ep.vec4 && n + 3 < p.N) {
+                    const f32x4 v = load_out4(crow + (int64_t)n * ep.c_cs, ok);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cin_pre[i][j][e] = v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cin_pre[i][j][e] = load_out(crow + (int64_t)min(n + e, p.N - 1) * ep.c_cs, ok);
+                }
+            }
+        }
+        }
+    };
+    if (PRE_CIN && ep.beta != 0.0f) {
+        if (ep.out_kind == OUT_F32) preload(std::integral_constant<int, OUT_F32>{});
+        else if (ep.out_kind == OUT_BF16) preload(std::integral_constant<int, OUT_BF16>{});
+        else preload(std::integral_constant<int, OUT_F16>{});
+    }
     __syncthreads();
     const int tile = tm * p.tiles_n + tn;
     if (tid == 0) is_last = take_last_ticket(p.counters + tile, S);
@@ -677,7 +721,7 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             }
         }
     }
-    finish_any();
+    finish_any(std::integral_constant<bool, PRE_CIN>{});
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
