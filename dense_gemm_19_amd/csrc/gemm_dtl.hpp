@@ -686,7 +686,7 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     __syncthreads();
     if (!is_last) return;
     // The sum runs over s = 0..S-1 in order, this workgroup's own partial
-    // included.  Loads go out in batches of QB splits x IB 16-row blocks (at
+    // included (from registers where own[] exists: the same values).  Loads go out in batches of QB splits x IB 16-row blocks (at
     // most 64 values in flight beside the accumulators), every load of a batch
     // before any add, so a batch costs one memory round trip; a batch running
     // past the last split re-reads split S-1 (unconditional loads keep the
@@ -696,6 +696,15 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     };
     constexpr int IB = TM < (8 / TN > 0 ? 8 / TN : 1) ? TM : (8 / TN > 0 ? 8 / TN : 1);
     constexpr int QB = 16 / (IB * TN) > 0 ? 16 / (IB * TN) : 1;
+    // This piece's own partial comes from a register copy, not from memory,
+    // where the registers allow (as for cin_pre): a 1/S smaller load volume.
+    f32x4 own[PRE_CIN ? TM : 1][PRE_CIN ? TN : 1];
+    if constexpr (PRE_CIN) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) own[i][j] = acc[i][j];
+    }
 #pragma unroll
     for (int i0 = 0; i0 < TM; i0 += IB) {
         for (int q0 = 0; q0 < S; q0 += QB) {
@@ -706,9 +715,14 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
 #pragma unroll
                 for (int i = 0; i < IB; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                    for (int j = 0; j < TN; ++j) {
+                        if (PRE_CIN && q == z) {
+                            v[qq][i][j] = own[PRE_CIN ? i0 + i : 0][PRE_CIN ? j : 0];
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[qq][i][j][e] = part(q, i0 + i, j, e);
+                            for (int e = 0; e < 4; ++e) v[qq][i][j][e] = part(q, i0 + i, j, e);
+                        }
+                    }
             }
 #pragma unroll
             for (int qq = 0; qq < QB; ++qq) {
