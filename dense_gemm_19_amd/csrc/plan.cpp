@@ -102,11 +102,15 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
         // within the CUs.  The score is the CUs kept busy, discounted for
         // unequal splits and for the bytes of 128-byte lines a row's slabs
         // touch beyond the row itself (a slab edge inside a line makes two
-        // workgroups fetch that line).  Among scores within 3% of the best the
-        // widest slab wins, then the fewest splits: measured on x.W1 (BF16,
-        // N = 14336, K = 4096, 256 CUs), 512-byte row pieces on 224 workgroups
-        // took 21.3 us, 448-byte pieces on 256 workgroups 23.8 us, 256-byte
-        // pieces 25.7 us and 128-byte pieces 34.6 us.
+        // workgroups fetch that line).  Among scores within 3% of the best: the
+        // fewest splits whose slab is at least 128 columns (256-byte row pieces;
+        // a split adds the partial sum's round trips at the end), else the
+        // widest slab.  Measured on x.W1 (BF16, N = 14336, K = 4096, 256 CUs):
+        // 448-byte pieces (slab edges inside lines) on 256 workgroups 23.8 us
+        // against 21.1 us for 896-byte pieces on line boundaries, 256-byte pieces
+        // (224 workgroups) 25.7 us, 128-byte pieces 34.6 us; on 8 grouped
+        // [1,512] x [512,4096] experts, 128-column slabs without a split 9.2 us
+        // against 10.1 us for 256-column slabs in 2 splits.
         const int64_t sweep = SKINNY_BN_SWEEP;
         const int64_t sweeps = cdiv(std::max<int64_t>(p.K, 1), sweep);
         const int64_t maxcols = mmax <= SKINNY_WIDE_MMAX ? SKINNY_BN_WIDE_COLS : SKINNY_BN_COLS;
@@ -137,7 +141,7 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
             S = std::min<int64_t>(forced, sweeps);
         } else {
             const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(sweeps / 2, d.cus));
-            struct Opt { int64_t S, cols; double score; };
+            struct Opt { int64_t S, cols; double score, eff; };
             std::vector<Opt> opts;
             double best = 0.0;
             for (int64_t s = 1; s <= smax; ++s) {
@@ -145,13 +149,21 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
                 if (geometry(s, kps, cols, slabs) != s) continue;   // the rounding gives another count
                 const double units = (double)(slabs * s);
                 const double busy = units / std::max<double>(1.0, std::ceil(units / d.cus));   // per wave of CUs
-                const double score = busy * ((double)sweeps / (double)(s * (kps / sweep))) * line_eff(cols, slabs);
-                opts.push_back({s, cols, score});
+                const double eff = line_eff(cols, slabs);
+                const double score = busy * ((double)sweeps / (double)(s * (kps / sweep))) * eff;
+                opts.push_back({s, cols, score, eff});
                 best = std::max(best, score);
             }
-            int64_t wide_cols = 0;
-            for (const Opt &o : opts)
-                if (o.score >= 0.97 * best && o.cols > wide_cols) { S = o.S; wide_cols = o.cols; }
+            // (slab edges on line boundaries first, at equal scores)
+            int64_t wide_cols = 0, pick = 0, pick_aligned = 0;
+            for (const Opt &o : opts) {                                  // in increasing S
+                if (o.score < 0.97 * best) continue;
+                if (pick_aligned == 0 && o.cols >= 128 && o.eff > 0.99) pick_aligned = o.S;
+                if (pick == 0 && o.cols >= 128) pick = o.S;
+                if (o.cols > wide_cols) { S = o.S; wide_cols = o.cols; }
+            }
+            if (pick_aligned > 0) S = pick_aligned;
+            else if (pick > 0) S = pick;
         }
         int64_t kps, cols, slabs;
         geometry(S, kps, cols, slabs);

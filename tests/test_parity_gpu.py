@@ -241,14 +241,16 @@ def test_skinny_bn(dg, M, nk):
     check(dg, c)
 
 
-@pytest.mark.parametrize("mnk", [(1, 14003, 2048), (4, 9003, 1000), (8, 5003, 1000), (2, 1003, 4096), (3, 301, 777)],
+@pytest.mark.parametrize("mnk", [(1, 14003, 2048), (1, 20003, 4096), (4, 14003, 4096), (4, 9003, 1000), (8, 5003, 1000),
+                                 (2, 1003, 4096), (3, 301, 777)],
                          ids=lambda t: "x".join(map(str, t)))
 def test_skinny_bn_ragged_slabs(dg, mnk):
     # N not a multiple of 8, B rows padded to a 16-byte pitch with NaN: in the
     # last column slab one lane's 8 columns straddle N (element loads), the lanes
     # past N and past the slab width read nothing of B, and any read of the
-    # padding would surface as NaN.  Slab widths from 64 to 440 columns, the
-    # 32-lane and the 64-lane row layouts, with and without K splits.
+    # padding would surface as NaN.  Slab widths from 64 to 512 columns, the
+    # 32-lane and the 64-lane row layouts (320 and 512 columns), with and
+    # without K splits.
     M, N, K = mnk
     c = synth.gemm_case(M, N, K, BF16, torch.float32, seed=M + N + K, b_layout="pad", pad=(8 - N % 8) % 8 + 8)
     kind, text = _plan_field(dg, c, "kind")
