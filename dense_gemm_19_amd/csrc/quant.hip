@@ -3,14 +3,19 @@
 // nearest with ties to an even code (include/dg.h states the operation and
 // cites the pages).
 //
-// One workgroup of 256 threads owns a 128 x 128 tile of X for block scales, or
-// a 64 x 128 tile for token scales (more, smaller workgroups: the loads of
-// later ones overlap the arithmetic of earlier ones).  Thread t holds the
-// 8-element chunk cc = t % 16 of rows r0 + 16 i, r0 = t / 16, so the 16 lanes
-// of a row block are adjacent: the row maxima come from four shuffle steps,
-// the tile maximum from two more and one LDS exchange between the four waves.  X is read once (16-byte loads where rows are K-contiguous) and the
-// codes of a chunk leave as one 8-byte store.  The work is a stream: 3 bytes
-// per element for 16-bit X, 5 for FP32.
+// One workgroup of 256 threads owns a tile of X: 128 x 128 for block scales,
+// 16 x 512 (four 128-wide K blocks) for token scales where K >= 512, else
+// 64 x 128.  Thread t holds the 8-element chunk cc = t % CPR of rows
+// r0 + (256 / CPR) i, r0 = t / CPR, with CPR = 16 chunks per row (128-column
+// tiles: each wave load covers 4 rows x 128 columns) or 64 (512-column tiles:
+// each wave load covers one row x 512 columns, 1 KB of 16-bit X, the row
+// piece width at which a streaming read of this part reaches its peak).  The
+// 16 lanes of a 128-wide row block are adjacent either way: the row maxima come
+// from four shuffle steps, the block maximum from two more and one LDS
+// exchange between the four waves.  X is read once (16-byte loads where rows
+// are K-contiguous) and the codes of a chunk leave as one 8-byte store; with
+// 512-column tiles a row's four token scales leave from four adjacent lanes.
+// The work is a stream: 3 bytes per element for 16-bit X, 5 for FP32.
 #include "dg.h"
 #include "device_common.hpp"
 #include "quant.hpp"
@@ -19,6 +24,9 @@ namespace dg {
 namespace {
 
 constexpr float E4M3_MAX = 448.0f;
+// Row steps per thread of the 512-column token tiles (16 x 512 tiles; measured
+// on 4096 x 4096 BF16: 8 x 512 15.2 us, 16 x 512 14.5 us, 32 x 512 18.1 us).
+constexpr int QRT = 4;
 
 // x / s rounded to nearest, given r = RN(1/s): t = RN(x * r) is within one ulp
 // of the quotient, the FMA residual x - t * s is exact, and one correction
@@ -66,20 +74,22 @@ __device__ __forceinline__ float chunk_value(const Chunk<XT> &c, int j) {
 // outside X (rows past M, or a tile past the last one).
 __device__ __attribute__((aligned(16))) const u32x4 g_qzero[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 
-// The thread's RT chunks of tile `tile`: rows r0 + 16 i of the tile's 16*RT rows,
-// columns 8 cc .. 8 cc + 7 of its 128; zeros outside X.  VEC (X rows
+// The thread's RT chunks of tile `tile`: rows r0 + RS i of the tile's RS*RT rows
+// (RS = 256 / CPR), columns 8 cc .. 8 cc + 7 of its 8 * CPR; zeros outside X.  VEC (X rows
 // K-contiguous with 16-byte aligned chunks, K a multiple of 8): one or two
 // 16-byte loads per chunk, every one issued (chunks outside X read the zero
 // block), with no branch, so the compiler's wait before the first use of a
 // tile counts exactly the loads issued after it.  Otherwise element loads.
-template <int XT, int RT, bool VEC>
+template <int XT, int RT, bool VEC, int CPR>
 __device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, int cc, Chunk<XT> (&buf)[RT]) {
-    const int mb = tile / p.tiles_k, kb = tile - mb * p.tiles_k;
-    const int c0 = kb * 128 + cc * 8;
+    constexpr int RS = 256 / CPR, TC = 8 * CPR;
+    const int tiles_kw = (p.K + TC - 1) / TC;
+    const int mb = tile / tiles_kw, kw = tile - mb * tiles_kw;
+    const int c0 = kw * TC + cc * 8;
     const int nvalid = min(8, p.K - c0);
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-        const int row = mb * 16 * RT + r0 + 16 * i;
+        const int row = mb * RS * RT + r0 + RS * i;
         const char *xr = p.X + (int64_t)row * p.x_rs;
         if constexpr (VEC) {
             const char *src = row < p.M && nvalid > 0 ? xr + (int64_t)c0 * (XT == DG_F32 ? 4 : 2)
@@ -106,11 +116,15 @@ __device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, 
 }
 
 // Quantize one tile from the thread's chunks: row maxima, scales, codes, stores.
-template <int XT, int RT>
+template <int XT, int RT, int CPR>
 __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, int r0, int cc,
                                            const Chunk<XT> (&buf)[RT], float *wave_max) {
-    const int mb = tile / p.tiles_k, kb = tile - mb * p.tiles_k;
-    const int c0 = kb * 128 + cc * 8;
+    constexpr int RS = 256 / CPR, TC = 8 * CPR;
+    static_assert(CPR == 16 || CPR == 64, "16 or 64 chunks per row");
+    const int tiles_kw = (p.K + TC - 1) / TC;
+    const int mb = tile / tiles_kw, kw = tile - mb * tiles_kw;
+    const int kb = kw * (CPR / 16) + (cc >> 4);   // this lane's 128-wide K block
+    const int c0 = kw * TC + cc * 8;
     const int nvalid = min(8, p.K - c0);
     // row maxima over the 16 lanes of each row block (out-of-range elements are 0)
     float s[RT];
@@ -127,8 +141,8 @@ __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, 
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             s[i] = fmaxf(s[i], 1e-12f) / E4M3_MAX;
-            const int row = mb * 16 * RT + r0 + 16 * i;
-            if (cc == 0 && row < p.M)
+            const int row = mb * RS * RT + r0 + RS * i;
+            if ((cc & 15) == 0 && row < p.M && kb * 128 < p.K)
                 *reinterpret_cast<float *>(reinterpret_cast<char *>(p.S) + (int64_t)row * p.s_rs +
                                            (int64_t)kb * p.s_cs) = s[i];
         }
@@ -150,7 +164,7 @@ __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, 
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-        const int row = mb * 16 * RT + r0 + 16 * i;
+        const int row = mb * RS * RT + r0 + RS * i;
         if (row >= p.M || nvalid <= 0) continue;
         const float r = 1.0f / s[i];
         float c[8];
@@ -172,38 +186,41 @@ __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, 
     }
 }
 
-// RT: 16-row groups per thread (8: 128 x 128 tiles; 4: 64 x 128, token scales
-// only).  Each workgroup walks tiles bid, bid + grid, ... with the next tile's
-// loads in flight while it quantizes and stores the current one, so that the
-// reads and writes of the whole grid overlap instead of running in two waves.
-template <int XT, int RT, bool VEC>
+// RT: chunks (row steps) per thread (CPR 16: 8 for 128 x 128 tiles, 4 for
+// 64 x 128 token tiles; CPR 64: 4 for 16 x 512 token tiles).  Each workgroup
+// walks tiles bid, bid + grid, ... with the next tile's loads in flight while
+// it quantizes and stores the current one, so that the reads and writes of the
+// whole grid overlap instead of running in two waves.
+template <int XT, int RT, bool VEC, int CPR>
 __global__ void __launch_bounds__(256) quant_fp8(QuantArgs p, int ntiles) {
     __shared__ float wave_max[2][4];   // (double-buffered: the next tile writes the other half)
-    const int t = threadIdx.x, cc = t & 15, r0 = t >> 4;
+    const int t = threadIdx.x, cc = t % CPR, r0 = t / CPR;
     Chunk<XT> b0[RT], b1[RT];
     // The loads of a tile past the last one are issued too: its rows lie past M,
     // so they read nothing and give zeros.  Unconditional loads keep the wait
     // before each quantization exact (a load under a condition makes the
     // compiler wait for every load in flight, the next tile's included).
     int tile = blockIdx.x;
-    load_tile<XT, RT, VEC>(p, tile, r0, cc, b0);
+    load_tile<XT, RT, VEC, CPR>(p, tile, r0, cc, b0);
     for (; tile < ntiles; tile += 2 * gridDim.x) {
         const int t1 = tile + gridDim.x, t2 = t1 + gridDim.x;
-        load_tile<XT, RT, VEC>(p, t1, r0, cc, b1);
-        quant_tile<XT, RT>(p, tile, t, r0, cc, b0, wave_max[0]);
+        load_tile<XT, RT, VEC, CPR>(p, t1, r0, cc, b1);
+        quant_tile<XT, RT, CPR>(p, tile, t, r0, cc, b0, wave_max[0]);
         if (t1 >= ntiles) break;
-        load_tile<XT, RT, VEC>(p, t2, r0, cc, b0);
-        quant_tile<XT, RT>(p, t1, t, r0, cc, b1, wave_max[1]);
+        load_tile<XT, RT, VEC, CPR>(p, t2, r0, cc, b0);
+        quant_tile<XT, RT, CPR>(p, t1, t, r0, cc, b1, wave_max[1]);
     }
 }
 
 }  // namespace
 
 hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream, int cus) {
-    // Token scales: 64 x 128 tiles; block scales need the whole 128 x 128 block
-    // in one workgroup.  A persistent grid of 2 workgroups per CU walks them.
-    const int rows = a.block ? 128 : 64;
-    const int64_t ntiles = (int64_t)((a.M + rows - 1) / rows) * a.tiles_k;
+    // Token scales: 16 x 512 tiles (64 x 128 where K < 512); block scales need
+    // the whole 128 x 128 block in one workgroup.  A persistent grid of 2
+    // workgroups per CU walks them.
+    const bool wide = !a.block && a.K >= 512;
+    const int rows = a.block ? 128 : wide ? 4 * QRT : 64, cols = wide ? 512 : 128;
+    const int64_t ntiles = (int64_t)((a.M + rows - 1) / rows) * ((a.K + cols - 1) / cols);
     // 2 workgroups per CU, each walking its tiles with the next tile's loads in
     // flight (measured: 1, 2, 3-4, 6, 8 per CU -> A 4096x4096 per token 18.3, 15.1,
     // 16.1, 16.0, 15.2 us; B 4096x7168 per block 25.8, 20.9, 22.1, 23.3, 22.4 us).
@@ -211,19 +228,23 @@ hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream, int
     const dim3 grid((unsigned)(ntiles < want ? ntiles : want)), block(256);
     const int n = (int)ntiles;
     const bool vec = a.x_vec && a.K % 8 == 0;
-#define DG_QUANT_LAUNCH(XT, RT)                                                                       \
+#define DG_QUANT_LAUNCH(XT, RT, CPR)                                                                  \
     do {                                                                                              \
-        if (vec) hipLaunchKernelGGL((quant_fp8<XT, RT, true>), grid, block, 0, stream, a, n);        \
-        else hipLaunchKernelGGL((quant_fp8<XT, RT, false>), grid, block, 0, stream, a, n);           \
+        if (vec) hipLaunchKernelGGL((quant_fp8<XT, RT, true, CPR>), grid, block, 0, stream, a, n);   \
+        else hipLaunchKernelGGL((quant_fp8<XT, RT, false, CPR>), grid, block, 0, stream, a, n);      \
     } while (0)
     if (a.block) {
-        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 8);
-        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 8);
-        else DG_QUANT_LAUNCH(DG_BF16, 8);
+        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 8, 16);
+        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 8, 16);
+        else DG_QUANT_LAUNCH(DG_BF16, 8, 16);
+    } else if (wide) {
+        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, QRT, 64);
+        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, QRT, 64);
+        else DG_QUANT_LAUNCH(DG_BF16, QRT, 64);
     } else {
-        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 4);
-        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 4);
-        else DG_QUANT_LAUNCH(DG_BF16, 4);
+        if (x_dtype == DG_F32) DG_QUANT_LAUNCH(DG_F32, 4, 16);
+        else if (x_dtype == DG_F16) DG_QUANT_LAUNCH(DG_F16, 4, 16);
+        else DG_QUANT_LAUNCH(DG_BF16, 4, 16);
     }
 #undef DG_QUANT_LAUNCH
     return hipGetLastError();

@@ -11,7 +11,7 @@ struct QuantArgs {
     char *Q; int64_t q_rs, q_cs;         // M x K E4M3 codes
     float *S; int64_t s_rs, s_cs;        // scales, byte strides
     int M, K;
-    int tiles_k;                         // ceil(K / 128); the grid is ceil(M / 128) * tiles_k
+    int tiles_k;                         // ceil(K / 128): the 128-wide K blocks (scale columns)
     int block;                           // 0: one scale per row and 128 K; 1: per 128 x 128
     int x_vec;                           // X rows K-contiguous, 16-byte aligned 8-element chunks
     int q_vec;                           // Q rows K-contiguous, 8-byte aligned 8-element chunks

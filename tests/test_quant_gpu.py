@@ -71,6 +71,11 @@ def test_strided_views(dg, mode):
     # X with a padded row pitch (odd element offset: the element path)
     xp = synth.place(synth.to_dtype(synth.draw(g, (130, 260), "normal", 1.0), torch.float16), "pad", pad=3)
     check(dg, xp, mode)
+    # K >= 512 (token scales: 512-column tiles) through the same strided views
+    x = synth.place(synth.to_dtype(synth.draw(g, (40, 1100), "normal", 1.0), torch.bfloat16), "col")
+    check(dg, x, mode, q_layout="col", s_layout="col")
+    xp = synth.place(synth.to_dtype(synth.draw(g, (37, 1031), "normal", 1.0), torch.float16), "pad", pad=3)
+    check(dg, xp, mode)
 
 
 def test_special_values(dg):
