@@ -127,6 +127,20 @@ def test_run_twice_bitwise(dg):
         assert torch.equal(x, y)
 
 
+def test_wide_and_narrow_slab_batches(dg):
+    # Streaming groups whose planned slabs are wider than 256 columns run in a
+    # launch of their own (the 64-lane row layout) beside the 32-lane batch of the
+    # same M class; one wide group has N = 9003 with B rows padded by NaN, so its
+    # last slab has a lane straddling N.
+    cases = [synth.gemm_case(1, 14336, 2048, BF16, BF16, seed=801, name="w0"),
+             synth.gemm_case(2, 1000, 700, BF16, F32, seed=802, name="n1"),
+             synth.gemm_case(1, 9003, 1024, BF16, BF16, seed=803, b_layout="pad", pad=13, name="w2"),
+             synth.gemm_case(3, 12000, 512, BF16, F32, seed=804, name="w3")]
+    _, text = check_grouped(dg, cases)
+    widths = [int(g.split("c")[-1]) for g in text.replace(" |", "").split("groups=")[1:] for g in g.split()[0].split(",")]
+    assert any(w > 256 for w in widths) and any(w <= 256 for w in widths), text
+
+
 def test_moe_full_precision_output(dg):
     cases = synth.moe_experts(E=8, M=1, K=512, N=4096, seed=108, out_dtype=F32)
     got, _ = check_grouped(dg, cases)
