@@ -11,7 +11,8 @@ every input already resident in HBM: W1 and the cache are rotated over enough
 distinct copies (>= 1 GiB in all) that neither the 256 MB Infinity Cache nor
 the L2 can serve a repeat.  The two products are independent, so each runs on
 its own HIP stream (both at the default priority): the cache product's 128
-one-wave workgroups fill CUs that the x.W1 grid (224 workgroups) leaves free.
+one-wave workgroups run beside the x.W1 grid (256 workgroups of 8 waves, one
+per CU, which leaves room for more waves on every CU).
 `value` is the step's algorithmic bytes (each operand read once, C written
 once) per second over K steps; `one_stream` repeats the measurement with both
 products on one stream, one after the other.
@@ -386,11 +387,16 @@ def time_config(dg, name, reps=None, trials=5, tune=False):
 
 
 def source_hash():
+    """Hash of the dominant kernel's sources with comments and blank space
+    removed, so that a change of comments alone keeps the measured traffic."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES + ["dense_gemm_19_amd/csrc/device_common.hpp",
                                "dense_gemm_19_amd/csrc/kernels.hpp"]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

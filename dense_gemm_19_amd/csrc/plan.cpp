@@ -89,7 +89,7 @@ bool skinny_ok(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
     const int mmax = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
     const bool no_vec = overrides().no_vec;
     // B N-contiguous: stream row pieces of B, a slab of at most 256 columns per
-    // workgroup.
+    // workgroup (512 in the 64-lane layout, M <= SKINNY_WIDE_MMAX).
     if (!no_vec && B.cols_contig() && B.cs == B.esize && B.align_ptr >= 16 && (p.K <= 1 || B.align_rs >= 16)) {
         pl.sk_kind = SK_BN;
         // Slabs x K splits should fill the CUs once: a CU streams at a bounded

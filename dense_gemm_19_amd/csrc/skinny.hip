@@ -11,15 +11,17 @@
 // article, section 4.5), so results are reproducible.
 //
 // SK_BN: B is N-contiguous (row-major [K][N], e.g. W1).  A workgroup of 8 waves
-//   owns a slab of p.cols <= 256 columns (2 * p.cols bytes of every row of B)
-//   and one split of K.  Lane (r, c) of a wave, r = lane/32, c = lane%32, owns
-//   columns 8c..8c+7 of the slab (lanes with 8c >= p.cols load nothing of B)
-//   and, in each 128-row sweep, the 8 consecutive rows 8*(2*wave + r) + u,
-//   u < 8: every load instruction of a wave reads two whole row pieces of the
-//   slab, and the A values a lane needs are 16-byte LDS reads.  The slab width
-//   is planned so that slabs x K splits fill the CUs once (x.W1, N = 14336:
-//   64 slabs of 224 columns x 4 splits = 256 workgroups; 256-column slabs
-//   would leave 32 of 256 CUs idle, and each CU streams at a bounded rate).
+//   owns a slab of p.cols columns and one split of K.  W = 32 lanes cover a row
+//   piece (slabs of at most 256 columns): lane (r, c), r = lane/32, c = lane%32,
+//   owns columns 8c..8c+7 of the slab and, in each 128-row sweep, the 8
+//   consecutive rows 8*(2*wave + r) + u, u < 8, so every load instruction of a
+//   wave reads two whole row pieces.  W = 64 (slabs of up to 512 columns, M <= 4):
+//   lane c owns columns 8c..8c+7 and the rows 8*wave + u of 64-row sweeps, one
+//   row piece of up to 1 KB per load instruction.  Lanes with 8c >= p.cols load
+//   nothing of B.  The A values a lane needs are 16-byte LDS reads.  The slab
+//   width and the K split are planned together so that slabs x splits fill the
+//   CUs once with whole 128-byte lines per row piece (x.W1, N = 14336: 32 slabs
+//   of 448 columns x 8 splits = 256 workgroups).
 //   A's K slice is staged in LDS as 16-bit values [m][k], with the first
 //   sweep's loads of B already in flight.  The two row groups of a wave are
 //   summed with a shuffle and the 8 waves through LDS, always in the same
