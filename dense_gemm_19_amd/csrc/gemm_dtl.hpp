@@ -538,7 +538,7 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     // would drop from two waves per SIMD to one); cin_pre[i][j][e] belongs to
     // element (i, j, e).  Unused otherwise.
     constexpr bool PRE_CIN = SPLIT && TM * TN <= 8;
-    float cin_pre[PRE_CIN ? TM : 1][PRE_CIN ? TN : 1][4];
+    float cin_pre[PRE_CIN ? TM : 1][PRE_CIN ? TN : 1][4] = {};
     auto finish = [&](auto OUTK, auto FUSED, auto PRE) __attribute__((always_inline)) {
         constexpr int ok = decltype(OUTK)::value;
         constexpr bool fused = decltype(FUSED)::value;
