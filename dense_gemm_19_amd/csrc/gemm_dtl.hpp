@@ -376,26 +376,30 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             // formed transposed, see mma), so it needs one row scale per 16-row
             // block: TM floats side by side in the stage's scale layout.
             const float *lsa = reinterpret_cast<const float *>(la + SA_OFF) + (lane & 15) * (BM / 16);
-            const float sb = reinterpret_cast<const float *>(la + SB_OFF)[(wn * WTN) >> 7];
-            float sc[TM];
-            if constexpr (TM % 4 == 0) {
+            const float *lsb = reinterpret_cast<const float *>(la + SB_OFF) + ((wn * WTN) >> 7);
+            float sc[TM], sb = 0.0f;
+            f32x4 sraw[TM % 4 == 0 ? TM / 4 : 1];
+            auto read_scales = [&]() __attribute__((always_inline)) {
+                sb = *lsb;
+                if constexpr (TM % 4 == 0) {
 #pragma unroll
-                for (int q = 0; q < TM; q += 4) {
-                    const int chunk = ((wm * TM + q) >> 2) ^ sa_swz<BM>(lane & 15);
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(lsa + 4 * chunk);
+                    for (int q = 0; q < TM; q += 4) {
+                        const int chunk = ((wm * TM + q) >> 2) ^ sa_swz<BM>(lane & 15);
+                        sraw[q / 4] = *reinterpret_cast<const f32x4 *>(lsa + 4 * chunk);
+                    }
+                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sc[q + e] = v[e] * sb;
+                    for (int q = 0; q < TM; ++q) {
+                        const int b = wm * TM + q;
+                        sc[q] = lsa[4 * ((b >> 2) ^ sa_swz<BM>(lane & 15)) + (b & 3)];
+                    }
                 }
-            } else {
+            };
+            auto scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
-                for (int q = 0; q < TM; ++q) {
-                    const int b = wm * TM + q;
-                    sc[q] = lsa[4 * ((b >> 2) ^ sa_swz<BM>(lane & 15)) + (b & 3)] * sb;
-                }
-            }
-            i32x8 fb[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = frag8<BMODE, BN>(lb, wn * WTN + 16 * j, lane);
+                for (int q = 0; q < TM; ++q)
+                    sc[q] = (TM % 4 == 0 ? sraw[TM % 4 == 0 ? q / 4 : 0][q % 4] : sc[q]) * sb;
+            };
             // Block sums over this 128-wide K block on the matrix cores, then
             // promotion into the FP32 accumulators with the scales applied once.
             // The promotion of block t runs after the matrix instructions of blocks
@@ -407,21 +411,49 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             constexpr int PL = AMODE == MNMAJ ? 2 : 4;   // promotion lag, in blocks
             // Each step is fenced (sched_barrier) so that the compiler keeps the
             // order written here: the matrix instruction of block t, then the
-            // promotion of block t - PL, whose sums are complete by then; left
-            // free, it pulls each block's promotion up behind its own matrix
-            // instruction and pads the wait with nops.  The A fragment of the
-            // next 16-row block is read TN blocks ahead of its first use.
+            // reads for later steps, then the promotion of block t - PL, whose
+            // sums are complete by then; left free, it pulls each block's
+            // promotion up behind its own matrix instruction and pads the wait
+            // with nops.  Reads are issued just ahead of their use, so that few
+            // are outstanding when a matrix instruction waits for its own (LDS
+            // reads complete in order): the first block's B and A fragments
+            // before the loop, B fragment j + 2 after block j's instruction (the
+            // B fragments then stay for the whole K block), the A fragment of the
+            // next 16-row block TN blocks ahead, and the scales after block 1,
+            // their products formed at step PL.
+            // Where A is M-contiguous its transposed reads hold more registers and
+            // this order spills: there every fragment and scale is read before the
+            // loop (EARLY), the A fragment of the next block ahead of the matrix
+            // instruction.
+            constexpr bool EARLY = AMODE == MNMAJ;
+            i32x8 fb[TN];
+            if constexpr (EARLY) {
+                read_scales();
+                scales();
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[j] = frag8<BMODE, BN>(lb, wn * WTN + 16 * j, lane);
+            } else {
+                fb[0] = frag8<BMODE, BN>(lb, wn * WTN, lane);
+            }
             i32x8 fa = frag8<AMODE, BM>(la, wm * WTM, lane), fa_next = fa;
+            if constexpr (!EARLY && TN > 1) fb[1] = frag8<BMODE, BN>(lb, wn * WTN + 16, lane);
             f32x4 blk[PL + 1];
 #pragma unroll
             for (int t = 0; t < TM * TN + PL; ++t) {
                 if (t < TM * TN) {
                     const int i = t / TN, j = t % TN;
-                    if (j == 0 && i + 1 < TM) fa_next = frag8<AMODE, BM>(la, wm * WTM + 16 * (i + 1), lane);
+                    if (EARLY && j == 0 && i + 1 < TM) fa_next = frag8<AMODE, BM>(la, wm * WTM + 16 * (i + 1), lane);
                     blk[t % (PL + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    if constexpr (!EARLY) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (i == 0 && j + 2 < TN) fb[j + 2] = frag8<BMODE, BN>(lb, wn * WTN + 16 * (j + 2), lane);
+                        if (t == 1 || (TM * TN == 1 && t == 0)) read_scales();
+                        if (j == 0 && i + 1 < TM) fa_next = frag8<AMODE, BM>(la, wm * WTM + 16 * (i + 1), lane);
+                    }
                     if (j == TN - 1) fa = fa_next;
                 }
+                if (!EARLY && t == PL) scales();
                 if (t >= PL) {
                     const int u = t - PL, pi = u / TN, pj = u % TN;
 #pragma unroll
