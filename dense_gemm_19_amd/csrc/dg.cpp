@@ -294,6 +294,12 @@ MfmaArgs make_mfma_args(const Problem &p, const Plan &pl, const Scratch &sc) {
 dg_status launch_plan(const Problem &p, const Plan &pl, const Scratch &sc, hipStream_t stream) {
     const Epilogue epi = make_epi(p);
     if (pl.path == Path::Noop) return DG_SUCCESS;
+    if (pl.split_n > 0) {   // column split: the two parts in stream order, one workspace
+        Problem lo, hi;
+        split_columns(p, pl.split_n, &lo, &hi);
+        const dg_status st = launch_plan(lo, *pl.part1, sc, stream);
+        return st != DG_SUCCESS ? st : launch_plan(hi, *pl.part2, sc, stream);
+    }
     if (pl.path == Path::Scale) {
         ScaleArgs s{epi, (int)p.M, (int)p.N};
         return launch_scale(s, stream) == hipSuccess ? DG_SUCCESS : DG_ERR_HIP;

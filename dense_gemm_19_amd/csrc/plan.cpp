@@ -1,6 +1,7 @@
 // plan.cpp -- see plan.hpp.
 #include "plan.hpp"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -346,7 +347,46 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
 
 Plan select_plan(const Problem &p, const Device &d) { return select_plan(p, d, PlanChoice()); }
 
-Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c) {
+namespace {
+
+int ptr_align(const char *p) {
+    const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+    int a = 1;
+    while (a < 16 && (v % (2 * a)) == 0) a *= 2;
+    return a;
+}
+
+void cut_columns(Mat &m, int64_t c0, int64_t n) {
+    m.ptr += c0 * m.cs;
+    m.cols = n;
+    m.align_ptr = ptr_align(m.ptr);
+}
+
+}  // namespace
+
+void split_columns(const Problem &p, int64_t n1, Problem *lo, Problem *hi) {
+    *lo = p;
+    *hi = p;
+    lo->N = n1;
+    hi->N = p.N - n1;
+    cut_columns(lo->B, 0, n1);
+    cut_columns(hi->B, n1, p.N - n1);
+    cut_columns(lo->C, 0, n1);
+    cut_columns(hi->C, n1, p.N - n1);
+    if (p.fp8) {
+        const int64_t nb = cdiv(p.N, 128), nb1 = n1 / 128;
+        cut_columns(lo->SB, 0, nb1);
+        cut_columns(hi->SB, nb1, nb - nb1);
+    }
+    if (p.has_bias) {
+        cut_columns(lo->bias, 0, n1);
+        cut_columns(hi->bias, n1, p.N - n1);
+    }
+}
+
+namespace {
+
+Plan select_plan_one(const Problem &p, const Device &d, const PlanChoice &c) {
     Plan pl;
     if (p.M == 0 || p.N == 0) { pl.path = Path::Noop; return pl; }
     if (p.alpha == 0.0f || p.K == 0) { pl.path = Path::Scale; return pl; }
@@ -360,6 +400,46 @@ Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c) {
     if (!(pl.path == Path::Mfma && pl.dtl))
         pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
     return pl;
+}
+
+}  // namespace
+
+Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c) {
+    Plan pl = select_plan_one(p, d, c);
+    // Column split of the built-in plan: where the grid of 256 x 256 tiles
+    // would end in a short wave (the direct kernel then took smaller tiles for
+    // FP8, or 256 x 256 with that wave for 16-bit inputs), but the columns up to
+    // the last multiple of 256 fill whole waves of 256 x 256 tiles (and fewer
+    // than 256 columns remain), those columns run on that tile and the
+    // remaining strip as a problem of its own (its K split spreads it over the
+    // CUs) right after.  FP8 4096 x 4224 x 4096: 256 whole 256 x 256 tiles, then
+    // a 4096 x 128 strip, instead of 128 x 128 tiles with a split tail; BF16
+    // 4096 x 4160: 256 tiles and a 4096 x 64 strip instead of 272 tiles, whose
+    // second wave of 16 would take as long as the first.
+    if (!(c == PlanChoice()) || overrides().force_tile >= 0 || overrides().force_splitk > 0 ||
+        pl.path != Path::Mfma || !pl.dtl || p.M < 256)
+        return pl;
+    if (pl.tile == T256x256) {   // (16-bit inputs take it whatever the last wave holds)
+        const int64_t nt = tile_count(p.M, p.N, T256x256);
+        if ((double)nt / (double)(cdiv(nt, d.cus) * d.cus) >= 0.9) return pl;
+    }
+    const int64_t n1 = p.N / 256 * 256;
+    if (n1 == 0 || n1 == p.N) return pl;
+    const int64_t nt1 = cdiv(p.M, 256) * (n1 / 256);
+    if (nt1 < d.cus || (double)nt1 / (double)(cdiv(nt1, d.cus) * d.cus) < 0.9 || tile_eff(p.M, n1, T256x256) < 0.9)
+        return pl;
+    Problem lo, hi;
+    split_columns(p, n1, &lo, &hi);
+    const Plan a = select_plan_one(lo, d, c), b = select_plan_one(hi, d, c);
+    if (!(a.path == Path::Mfma && a.dtl && a.tile == T256x256)) return pl;
+    Plan out = a;
+    out.split_n = n1;
+    out.ws_bytes = std::max(a.ws_bytes, b.ws_bytes);
+    out.counters = std::max(a.counters, b.counters);
+    out.splits = std::max(a.splits, b.splits);
+    out.part1 = std::make_shared<const Plan>(a);
+    out.part2 = std::make_shared<const Plan>(b);
+    return out;
 }
 
 namespace {
@@ -581,10 +661,11 @@ std::string describe_choice(const PlanChoice &c) {
     return b;
 }
 
+std::string describe_core(const Plan &pl);
+
 std::string describe(const Problem &p, const Plan &pl, const Device &d) {
     static const char *kinds[] = {"f16", "bf16", "f8e4m3"};
     static const char *outs[] = {"f32", "f16", "bf16"};
-    static const char *modes[] = {"KMAJ", "MNMAJ"};
     char buf[1024];
     int n = 0;
     auto add = [&](const char *fmt, auto... args) {
@@ -592,6 +673,29 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
     };
     add("M=%lld N=%lld K=%lld in=%s out=%s alpha=%g beta=%g", (long long)p.M, (long long)p.N,
         (long long)p.K, kinds[p.in_kind], outs[p.out_kind], (double)p.alpha, (double)p.beta);
+    if (pl.split_n > 0) {
+        add(" path=split_n n1=%lld ws=%zu | part1 {%s} | part2 {%s}", (long long)pl.split_n, pl.ws_bytes,
+            describe_core(*pl.part1).c_str(), describe_core(*pl.part2).c_str());
+    } else {
+        add("%s", describe_core(pl).c_str());
+        add(" ws=%zu", pl.ws_bytes);
+    }
+    add(" | A %lldx%lld rs=%lld cs=%lld | B %lldx%lld rs=%lld cs=%lld | C %lldx%lld rs=%lld cs=%lld",
+        (long long)p.A.rows, (long long)p.A.cols, (long long)p.A.rs, (long long)p.A.cs,
+        (long long)p.B.rows, (long long)p.B.cols, (long long)p.B.rs, (long long)p.B.cs,
+        (long long)p.C.rows, (long long)p.C.cols, (long long)p.C.rs, (long long)p.C.cs);
+    add(" | device %s cus=%d", d.arch, d.cus);
+    return std::string(buf, std::min<size_t>(n, sizeof buf - 1));
+}
+
+// The kernel-path part of a plan's description.
+std::string describe_core(const Plan &pl) {
+    static const char *modes[] = {"KMAJ", "MNMAJ"};
+    char buf[512];
+    int n = 0;
+    auto add = [&](const char *fmt, auto... args) {
+        if (n < (int)sizeof buf) n += std::snprintf(buf + n, sizeof buf - n, fmt, args...);
+    };
     switch (pl.path) {
     case Path::Noop: add(" path=noop"); break;
     case Path::Scale: add(" path=scale"); break;
@@ -612,12 +716,6 @@ std::string describe(const Problem &p, const Plan &pl, const Device &d) {
             pl.dtl ? 1 : pl.splits, pl.lds_bytes);
         break;
     }
-    add(" ws=%zu", pl.ws_bytes);
-    add(" | A %lldx%lld rs=%lld cs=%lld | B %lldx%lld rs=%lld cs=%lld | C %lldx%lld rs=%lld cs=%lld",
-        (long long)p.A.rows, (long long)p.A.cols, (long long)p.A.rs, (long long)p.A.cs,
-        (long long)p.B.rows, (long long)p.B.cols, (long long)p.B.rs, (long long)p.B.cs,
-        (long long)p.C.rows, (long long)p.C.cols, (long long)p.C.rs, (long long)p.C.cs);
-    add(" | device %s cus=%d", d.arch, d.cus);
     return std::string(buf, std::min<size_t>(n, sizeof buf - 1));
 }
 

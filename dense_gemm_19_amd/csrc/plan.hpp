@@ -11,6 +11,7 @@
 #pragma once
 #include <cstddef>
 #include <cstdint>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -68,6 +69,12 @@ struct Plan {
     size_t ws_bytes = 0;
     int counters = 0;         // split-K arrival counters the kernel needs (0 on entry)
     int lds_bytes = 0;
+    // Column split (split_n > 0): columns [0, split_n) run as part1 (256 x 256
+    // tiles filling whole waves of CUs), then columns [split_n, N) as part2, in
+    // stream order on the same workspace; the fields above are part1's, except
+    // ws_bytes, counters and splits, the larger of the two parts'.
+    int64_t split_n = 0;
+    std::shared_ptr<const Plan> part1, part2;
 };
 
 // A caller's (or the tuner's) choice among the plans the kernels implement;
@@ -87,6 +94,10 @@ struct PlanChoice {
 // DG_NO_VEC=1 (element-wise loads everywhere), DG_NO_DTL=1 (register-staged
 // tile loads only) and DG_NO_TAIL_SPLIT=1 (no split of the last wave's tiles),
 // read once per process.
+// The two parts of a column split: columns [0, n1) and [n1, N) of B, C, the
+// FP8 column scales (n1 a multiple of 128) and the bias.
+void split_columns(const Problem &p, int64_t n1, Problem *lo, Problem *hi);
+
 Plan select_plan(const Problem &p, const Device &d);
 Plan select_plan(const Problem &p, const Device &d, const PlanChoice &c);
 

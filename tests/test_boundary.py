@@ -220,7 +220,8 @@ def test_few_tile_k_split():
 
 def test_fp8_tile_choice():
     """FP8 takes the 256x256 tile where its tiles fill at least 3/4 of the CU waves,
-    else 128x128 (with the split tail where the last wave is short)."""
+    else 128x128 (with the split tail where the last wave is short), or a column
+    split where the columns up to the last multiple of 256 fill whole waves."""
     E4 = torch.float8_e4m3fn
 
     def fp8_plan(M, N, K):
@@ -229,8 +230,10 @@ def test_fp8_tile_choice():
                        torch.empty(M, N, dtype=torch.bfloat16), 1.0, 0.0, sa, sb)
     p = fp8_plan(4096, 7168, 4096)     # 448 tiles over 256 CUs: 7/8 of two waves
     assert field(p, "tile") == "256x256" and field(p, "splits") == "1", p
-    p = fp8_plan(4096, 4224, 4096)     # 272 tiles: the second wave would hold 16
-    assert field(p, "tile") == "128x128" and int(field(p, "dp_tiles")) > 0, p
+    p = fp8_plan(4096, 4224, 4096)     # 272 tiles: the second wave would hold 16; the first
+    # 4096 columns fill one wave of 256x256 tiles, the last 128 run as a strip of their own
+    assert field(p, "path") == "split_n" and field(p, "n1") == "4096" and field(p, "tile") == "256x256", p
+    assert p.split("part2 {")[1].split("}")[0].count("splits=") == 1, p
     p = fp8_plan(2048, 2048, 2048)     # 64 tiles of 256x256: too few
     assert field(p, "tile") == "128x128", p
 

@@ -87,6 +87,7 @@ PATHS = [
     (65, 200, 1000, "row", "row", ("path=mfma", "dtl=0", "splits=8")),
     (512, 640, 512, "row", "row", ("path=mfma", "dtl=1", "splits=1")),
     (384, 384, 1024, "row", "row", ("path=mfma", "dtl=1", "splits=2")),
+    (4096, 4160, 128, "row", "row", ("path=split_n", "n1=4096")),   # column split: bias of both parts
     (1000, 4104, 512, "col", "row", ("path=mfma", "dtl=1")),
 ]
 

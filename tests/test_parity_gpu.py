@@ -151,6 +151,41 @@ def test_fp8_256x256_integer_bitwise(dg):
     check(dg, c, expect_bitwise=True)     # the whole C
 
 
+@pytest.mark.parametrize("kind", ["fp8", "bf16"])
+def test_column_split_integer_bitwise(dg, kind):
+    # A column split: the first 4096 columns on 256x256 tiles (one whole wave of
+    # 256 CUs), the last 128 (FP8) or 64 (BF16) columns as a strip of their own,
+    # launched after it on the same workspace.  Integer-valued inputs (with
+    # power-of-two scales per block for FP8) give exact sums: every element of C
+    # bitwise the oracle's, so a column of either part computed, scaled or
+    # stored in the wrong place would show.
+    g = synth.rng(91 + len(kind))
+    M, K = 4096, 512
+    N = 4224 if kind == "fp8" else 4160
+    if kind == "fp8":
+        A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), torch.float32).to(E4M3)
+        B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), torch.float32).to(E4M3)
+        sa = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(M, K // 128)))).float()
+        sb = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(K // 128, -(-N // 128))))).float()
+        c = synth.Case("int_split_fp8", A, B, torch.full((M, N), float("nan")), 1.0, 0.0, sa, sb, rtol=1e-3)
+    else:
+        A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), BF16)
+        B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), BF16)
+        c = synth.Case("int_split_bf16", A, B, torch.full((M, N), float("nan")), 1.0, 0.0)
+    path, text = _plan_field(dg, c, "path")
+    assert path == "split_n" and "n1=4096" in text, text
+    check(dg, c, expect_bitwise=True)
+
+
+def test_column_split_alpha_beta(dg):
+    # The same split with alpha, beta and a strided C (every part reads and
+    # writes its own columns of C_in / C through the view's strides).
+    c = synth.gemm_case(4096, 4160, 128, BF16, torch.float32, seed=93, alpha=0.5, beta=-1.5, c_layout="pad")
+    path, text = _plan_field(dg, c, "path")
+    assert path == "split_n", text
+    check(dg, c, literal=True)
+
+
 def test_bf16_256x256_integer_bitwise_whole_c(dg):
     # The BF16 256x256 tile (loader waves): integer-valued inputs, every element
     # of C compared, FP32 and BF16 outputs bitwise equal to the oracle's.
@@ -363,8 +398,10 @@ def test_tail_split_integer_bitwise_and_repeatable(dg):
     assert torch.equal(d1, d2)
 
 
-def test_tail_split_workload_c5_tail(dg):
-    case = synth.config("c5_tail")      # FP8 4096 x 4224 x 4096: 1024 whole tiles, 32 split in 4
-    dp, text = _plan_field(dg, case, "dp_tiles")
-    assert int(dp) == 1024, text
-    check(dg, case)     # the whole C: whole tiles and split ones
+def test_workload_c5_tail(dg):
+    # FP8 4096 x 4224 x 4096: a column split, 256 whole 256x256 tiles (one wave),
+    # then the 4096 x 128 strip with its K split
+    case = synth.config("c5_tail")
+    path, text = _plan_field(dg, case, "path")
+    assert path == "split_n" and "n1=4096" in text, text
+    check(dg, case)     # the whole C: both parts
