@@ -244,6 +244,12 @@ void plan_mfma(const Problem &p, Plan &pl, const Device &d, const PlanChoice &c)
             // a ticket, partials read back by the last workgroup).
             tile = p.fp8 ? T64x128 : T64x64;
             if (p.M > 64 && !p.fp8 && tile_eff(p.M, p.N, T128x64) > tile_eff(p.M, p.N, tile) + 1e-9) tile = T128x64;
+        } else if (p.fp8 && p.N <= 128 && tile_count(p.M, p.N, T64x128) < d.cus) {
+            // A tall FP8 strip (the columns a column split leaves): 64x128 tiles
+            // span its columns, so A is read once, and its K split (below) fills
+            // the CUs.  Measured on 4096 x 128 x 4096: 64x128 in 4 splits 14.9 us,
+            // 128x64 in 4 15.4, 64x64 in 2 16.1, 128x128 in 4 19.3.
+            tile = T64x128;
         } else {
             // Enough rows for a compute-bound shape: the largest tile that still
             // gives every CU a tile, else the one giving the most tiles.  FP8 takes
