@@ -276,7 +276,7 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
 // The workgroup body.  t_direct >= 0: this workgroup computes tile t_direct of
 // p whole (the grouped kernel, which maps its grid itself); otherwise the tile
 // (and K piece) follows from blockIdx.x and gridDim.x as described above.
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL, bool SA4>
 __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_direct) {
     constexpr int NW = WGM * WGN;
     // Waves 0 .. NLD-1 issue the tile loads; NLD < NW leaves the others to
@@ -299,8 +299,13 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     static_assert(BM % 64 == 0 || !F8, "row scales are staged 64 per wave");
     static_assert(!F8 || NLD >= BM / 64, "row scales are staged by the loader waves");
     static_assert((NS - 2) * PER_FILL <= 63, "vmcnt range");
-    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    // SA4: FP8 row scales 4 K blocks at a time (see sa4_group below), in two
+    // buffers of [BM rows][4 blocks] floats; kernels with a two-stage ring.
+    static_assert(!SA4 || (F8 && NS == 2 && TM % 4 == 0), "SA4");
+    constexpr int SA4_BUF = BM * 16;
+    static_assert(NS * STAGE + (SA4 ? 2 * SA4_BUF : 0) <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
+    __shared__ __attribute__((aligned(16))) char sa4_ring[SA4 ? 2 * SA4_BUF : 16];
     __shared__ int is_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -357,19 +362,44 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     const int64_t a_kstep = (int64_t)KEL * p.a.k_stride, b_kstep = (int64_t)KEL * p.b.k_stride;
     const uint32_t ring_lds = lds_addr(ring);
 
+    // FP8 row scales, 4 K blocks per load (SA4).  The per-tile 4-byte
+    // load-to-LDS of a row scale touches a cache line of its own for every row
+    // of the tile (the A and B tiles take 2 lines per row).  Where the scales
+    // of a row are contiguous over K blocks (16-byte aligned rows, K a multiple
+    // of 4 blocks; the launch checks), lane i of wave w < BM/64 instead loads
+    // row 64 w + i's scales of the 4 blocks of K-block group g = kt / 4 with
+    // one 16-byte load-to-LDS, into buffer g % 2 of sa4_ring ([BM rows][4
+    // blocks]): a quarter of those requests.  Group g + 1 is loaded while group
+    // g's first block is computed (its buffer last served group g - 1, done by
+    // then); the prologue loads the first two groups.  Only with a two-stage
+    // ring: every wait there is for all of a wave's loads, so the loads per
+    // tile may vary.
+    const uint32_t sa4_off = SA4 ? (uint32_t)((int64_t)min(m0 + 64 * (wave % (F8 ? BM / 64 : 1)) + lane, p.M - 1) * p.sa_rs) : 0u;
+    const uint32_t sa4_lds = lds_addr(sa4_ring);
+    auto sa4_group = [&](int g) __attribute__((always_inline)) {   // K-block group g into its buffer
+        if (SA4 && wave_u < BM / 64)
+            lds_load16(reinterpret_cast<const char *>(p.sa) + (int64_t)g * 16, sa4_off,
+                       sa4_lds + (uint32_t)((g & 1) * SA4_BUF + 1024 * wave_u));
+    };
+
     auto fill = [&](int stage_idx, int kt) __attribute__((always_inline)) {   // K tile kt into a stage
         if (NLD < NW && wave_u >= NLD) return;
         const uint32_t st = ring_lds + (uint32_t)(stage_idx * STAGE);
         AIO::issue(st, a_src, a_org + kt * a_kstep, wave_u);
         BIO::issue(st + A_BYTES, b_src, b_org + kt * b_kstep, wave_u);
         if constexpr (F8) {
-            lds_load4(reinterpret_cast<const char *>(p.sa) + (int64_t)kt * p.sa_cs, sa_off,
-                      st + SA_OFF + 256 * (wave_u % (BM / 64)));
+            if constexpr (!SA4)
+                lds_load4(reinterpret_cast<const char *>(p.sa) + (int64_t)kt * p.sa_cs, sa_off,
+                          st + SA_OFF + 256 * (wave_u % (BM / 64)));
             lds_load4(reinterpret_cast<const char *>(p.sb) + (int64_t)kt * p.sb_rs, sb_off, st + SB_OFF);
+            // tile kt - 1, the first of its group g, is being computed: group g + 1
+            // (the prologue loaded it where g is the first group)
+            if (SA4 && (kt & 3) == 1 && ((kt - 1) >> 2) > (kt0 >> 2) && ((kt >> 2) + 1) * 4 < kt1)
+                sa4_group((kt >> 2) + 1);
         }
     };
 
-    auto compute = [&](const char *la) __attribute__((always_inline)) {
+    auto compute = [&](const char *la, int kt) __attribute__((always_inline)) {
         const char *lb = la + A_BYTES;
         if constexpr (F8) {
             // This lane's rows are wm * WTM + 16 i + lane % 16 (the products are
@@ -381,7 +411,13 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             f32x4 sraw[TM % 4 == 0 ? TM / 4 : 1];
             auto read_scales = [&]() __attribute__((always_inline)) {
                 sb = *lsb;
-                if constexpr (TM % 4 == 0) {
+                if constexpr (SA4) {
+                    // rows wm * WTM + 16 q + lane % 16 of block kt, from its group's buffer
+                    const float *g4 = reinterpret_cast<const float *>(sa4_ring + ((kt >> 2) & 1) * SA4_BUF) +
+                                      4 * (wm * WTM + (lane & 15)) + (kt & 3);
+#pragma unroll
+                    for (int q = 0; q < TM; ++q) sraw[q / 4][q % 4] = g4[64 * q];
+                } else if constexpr (TM % 4 == 0) {
 #pragma unroll
                     for (int q = 0; q < TM; q += 4) {
                         const int chunk = ((wm * TM + q) >> 2) ^ sa_swz<BM>(lane & 15);
@@ -510,7 +546,12 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
 #undef DG_VMCNT
     };
 
-    // prologue: the first NS - 1 tiles go out
+    // prologue: the first NS - 1 tiles go out (and, SA4, the row scales of the
+    // first two K-block groups)
+    if (SA4 && kt0 < kt1) {
+        sa4_group(kt0 >> 2);
+        if (((kt0 >> 2) + 1) * 4 < kt1) sa4_group((kt0 >> 2) + 1);
+    }
 #pragma unroll
     for (int q = 0; q + 1 < NS; ++q)
         if (kt0 + q < kt1) fill(q, kt0 + q);
@@ -527,7 +568,7 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int nxt = cur == 0 ? NS - 1 : cur - 1;
         if (kt + NS - 1 < kt1) fill(nxt, kt + NS - 1);
-        compute(ring + cur * STAGE);
+        compute(ring + cur * STAGE, kt);
     };
     // With NS = 2 and 4 waves the loop runs two tiles per trip, so that each
     // stage's LDS addresses are fixed offsets (immediates) rather than a
@@ -771,9 +812,9 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL>
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AMODE, int BMODE, bool SPLIT, int NL, bool SA4>
 __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl(MfmaArgs p) {
-    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, SPLIT, NL>(p, -1);
+    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, SPLIT, NL, SA4>(p, -1);
 }
 
 // Several problems of one tile configuration in one grid (the experts of an
@@ -795,25 +836,38 @@ __global__ void __launch_bounds__(64 * WGM * WGN) mfma_dtl_grouped(GroupedMfmaAr
     int *dst = reinterpret_cast<int *>(&p);
 #pragma unroll
     for (int i = 0; i < (int)(sizeof(MfmaArgs) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
-    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, false, NL>(p, u - ga.unit_begin[g]);
+    mfma_dtl_body<IN, BM, BN, WGM, WGN, NS, AMODE, BMODE, false, NL, false>(p, u - ga.unit_begin[g]);
 }
 
-template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL>
-hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL, bool SA4>
+hipError_t launch_t2(const MfmaArgs &a, hipStream_t s) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
     const int tiles = a.tiles_m * a.tiles_n;
     dim3 grid(tiles);
     if (a.splits > 1) {
         grid = dim3(a.dp_tiles + (tiles - a.dp_tiles) * a.splits);
         if constexpr (TM * TN <= 16) {
-            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true, NL>), grid, dim3(64 * WGM * WGN), 0, s, a);
+            hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, true, NL, SA4>), grid, dim3(64 * WGM * WGN), 0, s, a);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;   // no split K for this tile (the planner never asks)
         }
     }
-    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, NL>), grid, dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((mfma_dtl<IN, BM, BN, WGM, WGN, NS, AM, BMd, false, NL, SA4>), grid, dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
+}
+
+// FP8 kernels with a two-stage ring load 4 K blocks of row scales at once
+// where every row's scales are contiguous, 16-byte aligned and whole groups of
+// 4 K blocks (SA4 in the kernel body).
+template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL>
+hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
+    constexpr bool SA4_OK = IN == IN_F8 && NS == 2 && (BM / WGM / 16) % 4 == 0;
+    if constexpr (SA4_OK) {
+        if (a.sa_cs == 4 && a.sa_rs % 16 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0 && a.ktiles % 4 == 0)
+            return launch_t2<IN, BM, BN, WGM, WGN, NS, AM, BMd, NL, true>(a, s);
+    }
+    return launch_t2<IN, BM, BN, WGM, WGN, NS, AM, BMd, NL, false>(a, s);
 }
 
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int NL = 0>

@@ -135,16 +135,25 @@ def test_integer_inputs_bitwise(dg, kind):
     check(dg, cb, expect_bitwise=True)
 
 
-def test_fp8_256x256_integer_bitwise(dg):
+@pytest.mark.parametrize("k_sa", [(512, "row"), (1536, "row"), (640, "row"), (1536, "col")],
+                         ids=lambda v: f"K{v[0]}-SA{v[1]}")
+def test_fp8_256x256_integer_bitwise(dg, k_sa):
     # The FP8 256x256 tile (loader waves, promotion in registers): integer-valued
-    # codes with power-of-two scales give exact sums, so the output is bitwise
-    # the oracle's on every sampled row.
+    # codes with power-of-two scales, drawn per row and K block, give exact sums,
+    # so every element of C is bitwise the oracle's and a scale taken from the
+    # wrong row or K block shows.  Row scales are loaded 4 K blocks per load
+    # where each row's scales are contiguous and K is a multiple of 4 blocks
+    # (K 512: one group of 4 blocks; 1536: three, the two buffers reused), else
+    # one block per tile: K 640 (5 blocks), or column-major scales.
+    K, sa_layout = k_sa
     g = synth.rng(79)
-    M, N, K = 4096, 4096, 512
+    M, N = 4096, 4096
     A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), torch.float32).to(E4M3)
     B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), torch.float32).to(E4M3)
     sa = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(M, K // 128)))).float()
     sb = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(K // 128, N // 128)))).float()
+    if sa_layout == "col":
+        sa = sa.t().contiguous().t()
     c = synth.Case("int_fp8_256", A, B, torch.zeros(M, N), 1.0, 0.0, sa, sb, rtol=1e-3)
     tile, text = _plan_field(dg, c, "tile")
     assert tile == "256x256", text
@@ -366,6 +375,7 @@ def test_dtl_256_row_stores_misaligned_window(dg):
 TAIL_CASES = [
     ("fp8", 2512, 3312, 2048, "row"),      # 520 tiles of 128x128: 512 whole, 8 split in 2
     ("fp8", 2512, 3312, 2048, "col"),
+    ("fp8", 2512, 3312, 2560, "row"),      # 8 split in 2 of 10 K blocks: the second piece starts mid-group
     ("bf16", 2900, 2904, 2048, "row"),     # 529 tiles: 512 whole, 17 split in 4, ragged edges
     ("f16", 2900, 2904, 1024, "row"),      # 17 split in 2, beta = 1 and an FP32 C
 ]
