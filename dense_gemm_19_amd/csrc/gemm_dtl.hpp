@@ -299,13 +299,13 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     static_assert(BM % 64 == 0 || !F8, "row scales are staged 64 per wave");
     static_assert(!F8 || NLD >= BM / 64, "row scales are staged by the loader waves");
     static_assert((NS - 2) * PER_FILL <= 63, "vmcnt range");
-    // SA4: FP8 row scales 4 K blocks at a time (see sa4_group below), in two
-    // buffers of [BM rows][4 blocks] floats; kernels with a two-stage ring.
-    static_assert(!SA4 || (F8 && NS == 2 && TM % 4 == 0), "SA4");
-    constexpr int SA4_BUF = BM * 16;
-    static_assert(NS * STAGE + (SA4 ? 2 * SA4_BUF : 0) <= 160 * 1024, "LDS");
+    // SA4: FP8 row scales 4 K blocks at a time (see sa4_group below), in
+    // SA4_NB buffers of [BM rows][4 blocks] floats.
+    static_assert(!SA4 || (F8 && TM % 4 == 0), "SA4");
+    constexpr int SA4_BUF = BM * 16, SA4_NB = NS == 2 ? 2 : 4;
+    static_assert(NS * STAGE + (SA4 ? SA4_NB * SA4_BUF : 0) <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
-    __shared__ __attribute__((aligned(16))) char sa4_ring[SA4 ? 2 * SA4_BUF : 16];
+    __shared__ __attribute__((aligned(16))) char sa4_ring[SA4 ? SA4_NB * SA4_BUF : 16];
     __shared__ int is_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -369,17 +369,33 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
     // of 4 blocks; the launch checks), lane i of wave w < BM/64 instead loads
     // row 64 w + i's scales of the 4 blocks of K-block group g = kt / 4 with
     // one 16-byte load-to-LDS, into buffer g % 2 of sa4_ring ([BM rows][4
-    // blocks]): a quarter of those requests.  Group g + 1 is loaded while group
-    // g's first block is computed (its buffer last served group g - 1, done by
-    // then); the prologue loads the first two groups.  Only with a two-stage
-    // ring: every wait there is for all of a wave's loads, so the loads per
-    // tile may vary.
+    // blocks]): a quarter of those requests.  The prologue loads the first two
+    // groups.
+    //  - Two-stage ring (every wait there is for all of a wave's loads, so the
+    //    loads per tile may vary): 2 buffers; group g + 1 is loaded whole while
+    //    group g's first block is computed (its buffer last served group g - 1,
+    //    done by then).
+    //  - Deeper rings count each wave's loads per tile exactly: the fill of tile
+    //    kt keeps its one row-scale load, now lanes 16 j .. 16 j + 15 (j = kt % 4)
+    //    of a 16-byte load of group kt / 4 + 1: the 4 fills of a group load the
+    //    next group, a quarter of its rows each.  The fill of tile kt is issued
+    //    NS - 1 tiles ahead of its compute, so a group is written up to NS + 3
+    //    tiles before its first block is computed: 4 buffers, the one written
+    //    last served the group 4 before, done by then.
     const uint32_t sa4_off = SA4 ? (uint32_t)((int64_t)min(m0 + 64 * (wave % (F8 ? BM / 64 : 1)) + lane, p.M - 1) * p.sa_rs) : 0u;
     const uint32_t sa4_lds = lds_addr(sa4_ring);
     auto sa4_group = [&](int g) __attribute__((always_inline)) {   // K-block group g into its buffer
         if (SA4 && wave_u < BM / 64)
             lds_load16(reinterpret_cast<const char *>(p.sa) + (int64_t)g * 16, sa4_off,
-                       sa4_lds + (uint32_t)((g & 1) * SA4_BUF + 1024 * wave_u));
+                       sa4_lds + (uint32_t)((g & (SA4_NB - 1)) * SA4_BUF + 1024 * wave_u));
+    };
+    // rows 16 j .. 16 j + 15 of each wave's 64 of group g (past the last group:
+    // the last group again, the same values into its own buffer)
+    auto sa4_quarter = [&](int g, int j) __attribute__((always_inline)) {
+        g = min(g, (p.ktiles >> 2) - 1);
+        if ((lane >> 4) == j)
+            lds_load16(reinterpret_cast<const char *>(p.sa) + (int64_t)g * 16, sa4_off,
+                       sa4_lds + (uint32_t)((g & (SA4_NB - 1)) * SA4_BUF + 1024 * (wave_u % (BM / 64))));
     };
 
     auto fill = [&](int stage_idx, int kt) __attribute__((always_inline)) {   // K tile kt into a stage
@@ -391,10 +407,12 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
             if constexpr (!SA4)
                 lds_load4(reinterpret_cast<const char *>(p.sa) + (int64_t)kt * p.sa_cs, sa_off,
                           st + SA_OFF + 256 * (wave_u % (BM / 64)));
+            else if constexpr (NS > 2)
+                sa4_quarter((kt >> 2) + 1, kt & 3);
             lds_load4(reinterpret_cast<const char *>(p.sb) + (int64_t)kt * p.sb_rs, sb_off, st + SB_OFF);
-            // tile kt - 1, the first of its group g, is being computed: group g + 1
-            // (the prologue loaded it where g is the first group)
-            if (SA4 && (kt & 3) == 1 && ((kt - 1) >> 2) > (kt0 >> 2) && ((kt >> 2) + 1) * 4 < kt1)
+            // two stages: tile kt - 1, the first of its group g, is being computed:
+            // group g + 1 (the prologue loaded it where g is the first group)
+            if (SA4 && NS == 2 && (kt & 3) == 1 && ((kt - 1) >> 2) > (kt0 >> 2) && ((kt >> 2) + 1) * 4 < kt1)
                 sa4_group((kt >> 2) + 1);
         }
     };
@@ -413,7 +431,7 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
                 sb = *lsb;
                 if constexpr (SA4) {
                     // rows wm * WTM + 16 q + lane % 16 of block kt, from its group's buffer
-                    const float *g4 = reinterpret_cast<const float *>(sa4_ring + ((kt >> 2) & 1) * SA4_BUF) +
+                    const float *g4 = reinterpret_cast<const float *>(sa4_ring + ((kt >> 2) & (SA4_NB - 1)) * SA4_BUF) +
                                       4 * (wm * WTM + (lane & 15)) + (kt & 3);
 #pragma unroll
                     for (int q = 0; q < TM; ++q) sraw[q / 4][q % 4] = g4[64 * q];
@@ -857,12 +875,12 @@ hipError_t launch_t2(const MfmaArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// FP8 kernels with a two-stage ring load 4 K blocks of row scales at once
-// where every row's scales are contiguous, 16-byte aligned and whole groups of
-// 4 K blocks (SA4 in the kernel body).
+// FP8 kernels with a two-stage ring, and the 64x128 tile, load 4 K blocks of
+// row scales at once where every row's scales are contiguous, 16-byte aligned
+// and whole groups of 4 K blocks (SA4 in the kernel body).
 template <int IN, int BM, int BN, int WGM, int WGN, int NS, int AM, int BMd, int NL>
 hipError_t launch_t(const MfmaArgs &a, hipStream_t s) {
-    constexpr bool SA4_OK = IN == IN_F8 && NS == 2 && (BM / WGM / 16) % 4 == 0;
+    constexpr bool SA4_OK = IN == IN_F8 && (NS == 2 || BM == 64) && (BM / WGM / 16) % 4 == 0;
     if constexpr (SA4_OK) {
         if (a.sa_cs == 4 && a.sa_rs % 16 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0 && a.ktiles % 4 == 0)
             return launch_t2<IN, BM, BN, WGM, WGN, NS, AM, BMd, NL, true>(a, s);

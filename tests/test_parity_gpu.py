@@ -160,6 +160,28 @@ def test_fp8_256x256_integer_bitwise(dg, k_sa):
     check(dg, c, expect_bitwise=True)     # the whole C
 
 
+@pytest.mark.parametrize("mnk", [(128, 1024, 1536), (4096, 128, 2560), (128, 1024, 640)],
+                         ids=lambda v: "x".join(map(str, v)))
+def test_fp8_64x128_integer_bitwise(dg, mnk):
+    # The FP8 64x128 tile (six-stage ring) with its K split: integer-valued codes
+    # and power-of-two scales per row and K block, so every element of C is
+    # bitwise the oracle's.  128 x 1024 x 1536: 12 K blocks in 4 pieces of 3,
+    # most starting inside a group of 4 blocks, whose row scales the fills of
+    # the group before load a quarter at a time; 4096 x 128 x 2560 (a tall strip):
+    # 20 blocks in 2 pieces of 10; 128 x 1024 x 640: 5 blocks, one row scale per
+    # tile.
+    M, N, K = mnk
+    g = synth.rng(83 + K)
+    A = synth.to_dtype(synth.draw(g, (M, K), "int", 8), torch.float32).to(E4M3)
+    B = synth.to_dtype(synth.draw(g, (K, N), "int", 8), torch.float32).to(E4M3)
+    sa = torch.from_numpy(np.exp2(g.integers(-3, 4, size=(M, K // 128)))).float()
+    sb = torch.from_numpy(np.exp2(g.integers(-2, 3, size=(K // 128, N // 128)))).float()
+    c = synth.Case("int_fp8_64x128", A, B, torch.full((M, N), float("nan")), 1.0, 0.0, sa, sb, rtol=1e-3)
+    tile, text = _plan_field(dg, c, "tile")
+    assert tile == "64x128" and "splits=1 " not in text, text
+    check(dg, c, expect_bitwise=True)
+
+
 @pytest.mark.parametrize("kind", ["fp8", "bf16"])
 def test_column_split_integer_bitwise(dg, kind):
     # A column split: the first 4096 columns on 256x256 tiles (one whole wave of
