@@ -15,7 +15,11 @@
 // exchange between the four waves.  X is read once (16-byte loads where rows
 // are K-contiguous) and the codes of a chunk leave as one 8-byte store; with
 // 512-column tiles a row's four token scales leave from four adjacent lanes.
-// The work is a stream: 3 bytes per element for 16-bit X, 5 for FP32.
+// The work is a stream: 3 bytes per element for 16-bit X, 5 for FP32.  Both
+// the 16-byte loads of X and the 8-byte code stores are nontemporal (neither
+// is touched again by this kernel; measured on MI355X: 4096 x 4096 BF16 per
+// token 14.55 -> 12.87 us, 4096 x 7168 per block 20.9 -> 18.7 us; nontemporal
+// loads alone 14.3 and 19.8 us).
 #include "dg.h"
 #include "device_common.hpp"
 #include "quant.hpp"
@@ -96,7 +100,7 @@ __device__ __forceinline__ void load_tile(const QuantArgs &p, int tile, int r0, 
                                                       : reinterpret_cast<const char *>(g_qzero);
 #pragma unroll
             for (int h = 0; h < Chunk<XT>::W / 4; ++h) {
-                const u32x4 q = *(const __attribute__((address_space(1))) u32x4 *)(src + 16 * h);
+                const u32x4 q = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(src + 16 * h));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t w = q[j];   // (an element copied to a scalar before any bit cast)
@@ -175,7 +179,7 @@ __device__ __forceinline__ void quant_tile(const QuantArgs &p, int tile, int t, 
         const uint32_t hi = e4m3_codes4(c[4], c[5], c[6], c[7]);
         char *qr = p.Q + (int64_t)row * p.q_rs;
         if (nvalid == 8 && p.q_vec) {
-            *reinterpret_cast<uint64_t *>(qr + c0) = (uint64_t)lo | ((uint64_t)hi << 32);
+            __builtin_nontemporal_store((uint64_t)lo | ((uint64_t)hi << 32), reinterpret_cast<uint64_t *>(qr + c0));
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
