@@ -29,7 +29,8 @@ namespace {
 
 constexpr float E4M3_MAX = 448.0f;
 // Row steps per thread of the 512-column token tiles (16 x 512 tiles; measured
-// on 4096 x 4096 BF16: 8 x 512 15.2 us, 16 x 512 14.5 us, 32 x 512 18.1 us).
+// on 4096 x 4096 BF16: 8 x 512 15.2 us, 16 x 512 14.5 us, 32 x 512 18.1 us;
+// with nontemporal accesses 8 x 512 14.2 us, 16 x 512 13.0 us, 32 x 512 13.8 us).
 constexpr int QRT = 4;
 
 // x / s rounded to nearest, given r = RN(1/s): t = RN(x * r) is within one ulp
@@ -220,15 +221,15 @@ __global__ void __launch_bounds__(256) quant_fp8(QuantArgs p, int ntiles) {
 
 hipError_t launch_quant(int x_dtype, const QuantArgs &a, hipStream_t stream, int cus) {
     // Token scales: 16 x 512 tiles (64 x 128 where K < 512); block scales need
-    // the whole 128 x 128 block in one workgroup.  A persistent grid of 2
-    // workgroups per CU walks them.
+    // the whole 128 x 128 block in one workgroup.  A persistent grid walks them.
     const bool wide = !a.block && a.K >= 512;
     const int rows = a.block ? 128 : wide ? 4 * QRT : 64, cols = wide ? 512 : 128;
     const int64_t ntiles = (int64_t)((a.M + rows - 1) / rows) * ((a.K + cols - 1) / cols);
-    // 2 workgroups per CU, each walking its tiles with the next tile's loads in
-    // flight (measured: 1, 2, 3-4, 6, 8 per CU -> A 4096x4096 per token 18.3, 15.1,
-    // 16.1, 16.0, 15.2 us; B 4096x7168 per block 25.8, 20.9, 22.1, 23.3, 22.4 us).
-    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 2;
+    // 4 (token scales) or 2 (block scales) workgroups per CU, each walking its
+    // tiles with the next tile's loads in flight (measured with nontemporal
+    // accesses: 1, 2, 4 per CU -> A 4096x4096 per token 16.8, 12.9, 12.5 us; B
+    // 4096x7168 per block 24.1, 18.7, 20.1 us).
+    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * (a.block ? 2 : 4);
     const dim3 grid((unsigned)(ntiles < want ? ntiles : want)), block(256);
     const int n = (int)ntiles;
     const bool vec = a.x_vec && a.K % 8 == 0;
