@@ -160,6 +160,16 @@ def test_fp8_256x256_integer_bitwise(dg, k_sa):
     check(dg, c, expect_bitwise=True)     # the whole C
 
 
+def test_fp8_256x256_ragged_m_grouped_scales(dg):
+    # The FP8 256x256 tile with an M edge inside its last tile row (4000 = 15 x 256
+    # + 160) and row scales loaded 4 K blocks at a time (K 1024: two groups): the
+    # rows past M load the last row's scales, and their products are never stored.
+    c = synth.fp8_case(4000, 7168, 1024, seed=4001, out_dtype=torch.float32, beta=0.5)
+    tile, text = _plan_field(dg, c, "tile")
+    assert tile == "256x256", text
+    check(dg, c, literal=True)
+
+
 @pytest.mark.parametrize("mnk", [(128, 1024, 1536), (4096, 128, 2560), (128, 1024, 640)],
                          ids=lambda v: "x".join(map(str, v)))
 def test_fp8_64x128_integer_bitwise(dg, mnk):
