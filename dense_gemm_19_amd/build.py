@@ -25,10 +25,11 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 # Per-source extra flags.  The FP8 kernels promote each matrix-core block sum on
 # the vector ALUs; the VGPR form of the MFMA instructions lets those sums land
 # where the ALUs can use them (no copies out of accumulation registers).
-EXTRA_FLAGS = {"gemm_dtl_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA_FLAGS = {"gemm_dtl_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "gemm_dtl_f8s.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
-HIP_SOURCES = ["gemm_mfma.hip", "gemm_dtl_f16.hip", "gemm_dtl_bf16.hip", "gemm_dtl_f8.hip", "skinny.hip",
+HIP_SOURCES = ["gemm_mfma.hip", "gemm_dtl_f16.hip", "gemm_dtl_bf16.hip", "gemm_dtl_f8.hip", "gemm_dtl_f8s.hip", "skinny.hip",
                "epilogue.hip", "calib.hip", "quant.hip", "noalloc.hip"]
 HOST_SOURCES = ["view.cpp", "plan.cpp", "dg.cpp", "gemm_dtl.cpp"]
 

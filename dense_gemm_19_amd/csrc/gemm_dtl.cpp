@@ -5,7 +5,8 @@ namespace dg {
 
 hipError_t launch_mfma_dtl_f16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
 hipError_t launch_mfma_dtl_bf16(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
-hipError_t launch_mfma_dtl_f8(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
+hipError_t launch_mfma_dtl_f8_two_stage(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
+hipError_t launch_mfma_dtl_f8_deep(int tile, int a_mode, int b_mode, const MfmaArgs &args, hipStream_t stream);
 
 hipError_t launch_mfma_dtl_grouped_f16(int tile, int a_mode, int b_mode, const GroupedMfmaArgs &args, int units,
                                      hipStream_t stream);
@@ -19,7 +20,9 @@ hipError_t launch_mfma_dtl(int in_kind, int tile, int a_mode, int b_mode, const 
     switch (in_kind) {
     case IN_F16: return launch_mfma_dtl_f16(tile, a_mode, b_mode, args, stream);
     case IN_BF16: return launch_mfma_dtl_bf16(tile, a_mode, b_mode, args, stream);
-    case IN_F8: return launch_mfma_dtl_f8(tile, a_mode, b_mode, args, stream);
+    case IN_F8:   // (256x256 and 128x128, the two-stage tiles, in one unit; the others in another)
+        return tile == T256x256 || tile == T128x128 ? launch_mfma_dtl_f8_two_stage(tile, a_mode, b_mode, args, stream)
+                                                    : launch_mfma_dtl_f8_deep(tile, a_mode, b_mode, args, stream);
     }
     return hipErrorInvalidValue;
 }

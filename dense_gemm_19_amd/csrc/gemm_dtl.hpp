@@ -932,6 +932,26 @@ hipError_t launch_tiles(int tile, int am, int bm, const MfmaArgs &a, hipStream_t
     return hipErrorInvalidValue;
 }
 
+// launch_tiles in two parts, the two-stage tiles (256x256, 128x128) and the
+// others, so that one input type's kernels can be compiled as two translation
+// units side by side.
+template <int IN, bool TWO_STAGE>
+hipError_t launch_tiles_part(int tile, int am, int bm, const MfmaArgs &a, hipStream_t s) {
+    if constexpr (TWO_STAGE) {
+        switch (tile) {
+        case T256x256: return launch_modes<IN, 256, 256, 2, 4, 2, 4>(am, bm, a, s);
+        case T128x128: return launch_modes<IN, 128, 128, 2, 2, 2>(am, bm, a, s);
+        }
+    } else {
+        switch (tile) {
+        case T128x64: return launch_modes<IN, 128, 64, 2, 2, 6>(am, bm, a, s);
+        case T64x64: return launch_modes<IN, 64, 64, 2, 2, 8>(am, bm, a, s);
+        case T64x128: return launch_modes<IN, 64, 128, 1, 4, 6>(am, bm, a, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 // The grouped kernel with the tile configurations of launch_tiles.
 template <int IN>
 hipError_t launch_grouped_tiles(int tile, int am, int bm, const GroupedMfmaArgs &a, int units, hipStream_t s) {
