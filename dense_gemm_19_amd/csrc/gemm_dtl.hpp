@@ -1,5 +1,5 @@
 // gemm_dtl.hpp -- matrix-core GEMM for gfx950 with direct HBM -> LDS tile loads
-// (templates; instantiated per input type by gemm_dtl_{f16,bf16,f8}.hip).
+// (templates; instantiated per input type by gemm_dtl_{f16,bf16,f8,f8s}.hip).
 //
 // Same computation as gemm_mfma.hip (C = alpha * A * B + beta * C, FP32
 // accumulation, and the FP8 E4M3 variant whose per-token and per-128x128-block
