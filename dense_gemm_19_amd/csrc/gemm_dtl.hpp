@@ -364,13 +364,13 @@ __device__ __forceinline__ void mfma_dtl_body(const MfmaArgs &p, const int t_dir
 
     // FP8 row scales, 4 K blocks per load (SA4).  The per-tile 4-byte
     // load-to-LDS of a row scale touches a cache line of its own for every row
-    // of the tile (the A and B tiles take 2 lines per row).  Where the scales
-    // of a row are contiguous over K blocks (16-byte aligned rows, K a multiple
-    // of 4 blocks; the launch checks), lane i of wave w < BM/64 instead loads
-    // row 64 w + i's scales of the 4 blocks of K-block group g = kt / 4 with
-    // one 16-byte load-to-LDS, into buffer g % 2 of sa4_ring ([BM rows][4
-    // blocks]): a quarter of those requests.  The prologue loads the first two
-    // groups.
+    // of the tile (the A and B tiles of a K tile take about 2 lines per tile
+    // row).  Where the scales of a row are contiguous over K blocks (16-byte
+    // aligned rows, K a multiple of 4 blocks; the launch checks), lane i of
+    // wave w < BM/64 instead loads row 64 w + i's scales of the 4 blocks of
+    // K-block group g = kt / 4 with one 16-byte load-to-LDS, into buffer
+    // g % SA4_NB of sa4_ring ([BM rows][4 blocks]): a quarter of those
+    // requests.  The prologue loads the first two groups.
     //  - Two-stage ring (every wait there is for all of a wave's loads, so the
     //    loads per tile may vary): 2 buffers; group g + 1 is loaded whole while
     //    group g's first block is computed (its buffer last served group g - 1,
